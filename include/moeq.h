@@ -1,0 +1,187 @@
+/*
+ * moeq.h -- C ABI of the block-scaled low-bit MoE decode library (MI355X, gfx950).
+ *
+ * The operation: a mixture-of-experts FFN layer whose expert weights are stored
+ * as block-scaled low-bit codes.  For each token the router logits pick the k
+ * best experts (top-k), their gate weights are the softmax of the k picked
+ * logits, each picked expert runs a SwiGLU FFN (gate | up projections, SiLU of
+ * the gate times the up, down projection) and the results are summed with
+ * those weights, plus an always-on shared expert with weight 1.
+ *
+ * Where each piece is stated (the pages, by title and section):
+ *  - weight formats: knivesysl README, "formats" (six-bit e2m3 values with a
+ *    power-of-two scale per 128 weights; four-bit nvfp4 values with a scale per
+ *    16) and "key flags" (the 4-bit e2m1 weight tier); colibri README,
+ *    "DeepSeek V4" (UE8M0 block scales, fp8-e4m3).
+ *  - routing and the shared expert: Strata docs/INTEL.md, "The engine itself on
+ *    Intel" (the router_top10 and shared_expert kernels); colibri README,
+ *    "DeepSeek V4" (routed experts plus one shared expert, top-k).
+ *  - the expert FFN split as gate | up then down: nextsycl README, "What it
+ *    does" and "Lessons learned".
+ *  - batched decode rows that must each equal their own one-row pass: nextsycl
+ *    README, "What it does" (several requests at once) and "Lessons learned".
+ *  - a native library behind a C ABI, loaded from Python: knivesysl README,
+ *    introduction; errors that name the failing operation: its "current
+ *    benchmark" section.
+ *
+ * Data layout (all row-major, every row contiguous; codes and scales planar):
+ *   MOE_FMT_E2M1_E4M3_B16   codes  [rows][cols/2]   element j in byte j>>1,
+ *                                                    low nibble = even element
+ *                           scales [rows][cols/16]  fp8 e4m3 (OCP "FN": bias 7,
+ *                                                    no Inf, 0x7F/0xFF = NaN)
+ *   MOE_FMT_E2M3_UE8M0_B128 codes  [rows][3*cols/4] element j in bits
+ *                                                    [6j, 6j+6) of the row read
+ *                                                    as a little-endian bit string
+ *                           scales [rows][cols/128] UE8M0: value 2^(b-127)
+ *   Weight W[r][j] = value(code) * value(scale[r][j / block]); e2m1 and e2m3
+ *   have one sign bit, two exponent bits of bias 1 and 1 or 3 mantissa bits,
+ *   with subnormals at exponent field 0 and no Inf/NaN codes.
+ *   An expert's w13 is [2*inter][hidden]: rows 0..inter-1 are the gate
+ *   projection, rows inter..2*inter-1 the up projection.  w2 is
+ *   [hidden][inter].  Routed experts are stacked: expert e's w13 codes begin
+ *   at w13_codes + e * 2*inter * code_row_bytes(hidden), and so on.
+ *   Activations x are bf16 [T][hidden]; logits fp32 [T][n_experts]; outputs
+ *   bf16 (or fp32 with MOE_OUT_F32) [T][hidden].
+ *
+ * Conventions for every call:
+ *  - Pointers to data are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *    unless stated otherwise; descriptor structs are host memory, read only
+ *    during the call.  The caller owns every buffer.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns; inputs must stay alive and unchanged until the
+ *    stream has passed the call.  No call allocates, frees or synchronises.
+ *  - Validation happens before anything is enqueued: on a negative return
+ *    nothing was enqueued, outputs are untouched, and moe_last_error() returns
+ *    text naming the argument and the rule it broke (thread-local).
+ *  - Device pointers must be 16-byte aligned; workspaces 256-byte aligned.
+ *  - Arithmetic: weights are decoded exactly, products and sums are formed in
+ *    fp32, the SiLU and the softmax in fp32, and the output is rounded to bf16
+ *    once (round to nearest even).  Routing compares the raw fp32 logits and
+ *    is bit-exact: larger logit first, equal logits (+0 == -0) by lower expert
+ *    index, NaN below every number.  A token's result does not depend on which
+ *    other tokens share the call.
+ *  - The library keeps no state between calls except constant tables.  Calls
+ *    on different streams need different workspaces; they are otherwise
+ *    reentrant.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* an argument breaks a documented rule */
+    MOE_EUNSUPPORTED = -2,  /* valid, but outside what this build implements */
+    MOE_EWORKSPACE = -3,    /* workspace missing, misaligned or too small */
+    MOE_EHIP = -4,          /* a HIP runtime call failed (text holds its error) */
+    MOE_EKERNEL = -5        /* a kernel's bounded wait expired (moe_workspace_status) */
+};
+
+/* Weight formats. */
+enum {
+    MOE_FMT_E2M1_E4M3_B16 = 1,    /* 4-bit e2m1, one fp8-e4m3 scale per 16 weights */
+    MOE_FMT_E2M3_UE8M0_B128 = 2   /* 6-bit e2m3, one UE8M0 (power-of-two) scale per 128 */
+};
+
+/* Flags. */
+enum {
+    MOE_OUT_F32 = 1,        /* write the output as fp32 (the value before bf16 rounding) */
+    MOE_DEBUG_SPIN_LIMIT = 1 << 30  /* test hook: inter-workgroup waits give up almost at once,
+                                       so the MOE_EKERNEL path can be exercised; output invalid */
+};
+
+/* Limits. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_TOKENS 65536
+#define MOE_MAX_GEMV_BATCH 8
+#define MOE_MAX_DIM 32768        /* hidden, inter, rows and cols */
+
+/* A block-scaled matrix [rows][cols]; y = W x reduces over cols.
+ * cols must be a multiple of 32 (e2m1) or 128 (e2m3). */
+typedef struct moe_qmat {
+    int32_t fmt;
+    int32_t rows;
+    int32_t cols;
+    int32_t reserved;        /* must be 0 */
+    const void *codes;       /* device, rows * code_row_bytes(cols) bytes */
+    const void *scales;      /* device, rows * scale_row_bytes(cols) bytes */
+} moe_qmat;
+
+/* One MoE layer.  hidden and inter (and shared_inter when nonzero) must be
+ * multiples of 32 (e2m1) or 128 (e2m3). */
+typedef struct moe_layer {
+    int32_t fmt;
+    int32_t hidden;          /* H */
+    int32_t inter;           /* I of every routed expert */
+    int32_t n_experts;       /* E, 1..MOE_MAX_EXPERTS */
+    int32_t top_k;           /* k, 1..min(E, MOE_MAX_TOPK) */
+    int32_t shared_inter;    /* I of the shared expert; 0 = no shared expert */
+    const void *w13_codes, *w13_scales;   /* [E][2I][H] */
+    const void *w2_codes, *w2_scales;     /* [E][H][I]  */
+    const void *sh13_codes, *sh13_scales; /* [2*shared_inter][H] (NULL if none) */
+    const void *sh2_codes, *sh2_scales;   /* [H][shared_inter]   (NULL if none) */
+} moe_layer;
+
+/* Top-k routing (the router_top10 step of Strata docs/INTEL.md, "The engine
+ * itself on Intel", for any k).
+ *   logits: device fp32 [T][E];  idx: device int32 [T][k];  w: device fp32 [T][k]
+ * idx[t] holds the k selected experts in rank order; w[t][r] =
+ * exp(l_r - l_0) / sum_s exp(l_s - l_0) over the selected logits, so the k
+ * weights sum to 1.  Limits: 1 <= T <= MOE_MAX_TOKENS, 1 <= E <=
+ * MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK). */
+int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w, void *stream);
+
+/* Bytes of workspace moe_layer_decode / moe_expert_ffn_q need for T tokens
+ * (*bytes is host memory).  The workspace must be zeroed once after
+ * allocation; the kernels leave its counters at zero on return. */
+int moe_layer_workspace_bytes(const moe_layer *L, int T, size_t *bytes);
+
+/* One expert's SwiGLU FFN on M rows of x (nextsycl README, "What it does":
+ * gate | up, then down).
+ *   expert: 0..E-1 for a routed expert, -1 for the shared expert
+ *   x: device bf16 [M][H];  y: device [M][H], bf16 or fp32 (MOE_OUT_F32)
+ *   ws: device workspace of at least moe_layer_workspace_bytes(L, M). */
+int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void *y, int flags,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer for T tokens: route, group the (token, expert) pairs by
+ * expert, run every selected expert once over its tokens, and combine
+ *   out[t] = sum_{r<k} w[t][r] * FFN_{idx[t][r]}(x_t) + FFN_shared(x_t)
+ * in that order.  idx_out (int32 [T][k]) and w_out (fp32 [T][k]) receive the
+ * routing when not NULL.  T <= 16 runs as one kernel launch (decode); larger
+ * T runs the grouped-GEMM prefill path (bf16 matrix cores after exact
+ * dequantisation in LDS). */
+int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int T, void *out,
+                     int32_t *idx_out, float *w_out, int flags, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Dense block-scaled GEMV: y[b] = W x[b] for B tokens sharing every decoded
+ * weight (knivesysl README, "formats": the fp6 projections).
+ *   x: device bf16 [B][cols];  y: device [B][rows], bf16 or fp32 (MOE_OUT_F32)
+ *   1 <= B <= MOE_MAX_GEMV_BATCH. */
+int dense_gemv_q(const moe_qmat *W, const void *x, int B, void *y, int flags, void *stream);
+
+/* Reads (synchronously, on `stream`) and clears the error word a kernel sets
+ * in the workspace when a bounded inter-workgroup wait expires.  Returns
+ * MOE_OK, MOE_EKERNEL, or a negative validation/HIP code. */
+int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
+
+/* Text of the last non-OK return on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

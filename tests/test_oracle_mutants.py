@@ -1,0 +1,179 @@
+"""Planted mistakes in copies of the oracle's source must each fail a pin.
+
+Each mutant is the oracle with one plausible slip (a wrong bias, nibble or bit
+order, scale index, tie-break, dropped term, swapped operand ...).  The copy
+is compiled on the CPU into a temporary library and run through a battery of
+the pins; the test passes when at least one pin rejects every mutant."""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+from scipy.special import expit, softmax
+
+import oracle
+import synth
+from helpers import read_packing_examples, read_table
+from synth.configs import MoEConfig
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+MUTANTS = {
+    "e2m1_bias": ("minifloat(c, 2, 1, 1)", "minifloat(c, 2, 1, 2)"),
+    "e2m3_fields": ("minifloat(c, 2, 3, 1)", "minifloat(c, 3, 2, 1)"),
+    "e4m3_bias": ("minifloat(b, 4, 3, 7)", "minifloat(b, 4, 3, 8)"),
+    "e4m3_nan": ("(b & 0x7F) == 0x7F", "(b & 0x7F) == 0x7E"),
+    "subnormal_exp": ("ldexp((double)m / (double)(1u << mbits), 1 - bias)",
+                      "ldexp((double)m / (double)(1u << mbits), -bias)"),
+    "nibble_order": ("(j & 1) ? (b >> 4) : (b & 0x0F)", "(j & 1) ? (b & 0x0F) : (b >> 4)"),
+    "e2m3_bit_order": ("& 1) << t;", "& 1) << (5 - t);"),
+    "scale_block": ("srow[j / 16]", "srow[j / 32]"),
+    "ue8m0_bias": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
+    "bf16_widen": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
+    "gemv_last_col": ("for (int64_t j = 0; j < cols; ++j) acc += weight_at(fmt, crow, srow, j) * bf16_value(x[j]);",
+                      "for (int64_t j = 0; j < cols - 1; ++j) acc += weight_at(fmt, crow, srow, j) * bf16_value(x[j]);"),
+    "tie_break": ("    if (la < lb) return 0;\n    return a < b;", "    if (la < lb) return 0;\n    return a > b;"),
+    "nan_order": ("return nb;", "return na;"),
+    "softmax_no_norm": ("w[t * k + r] = exp((double)l[idx[t * k + r]] - l0) / z;",
+                        "w[t * k + r] = exp((double)l[idx[t * k + r]] - l0);"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "gate_up_swap": ("h[i] = oracle_silu(g) * u;", "h[i] = oracle_silu(u) * g;"),
+    "up_rows": ("w13c + (I + i) * cbH, w13s + (I + i) * sbH", "w13c + i * cbH, w13s + i * sbH"),
+    "shared_weight": ("for (int64_t q = 0; q < n_out; ++q) o[q] += y[q];",
+                      "for (int64_t q = 0; q < n_out; ++q) o[q] += 0.5 * y[q];"),
+    "drop_rank0": ("for (int64_t r = 0; r < k; ++r) {\n            int32_t e",
+                   "for (int64_t r = 1; r < k; ++r) {\n            int32_t e"),
+}
+
+CFG = MoEConfig("mut", tokens=2, hidden=128, experts=4, top_k=2, inter=64, shared_inter=64)
+
+
+def _pin_tables():
+    t = oracle.tables()
+    g1, g3 = read_table("e2m1_values.txt"), read_table("e2m3_values.txt")
+    assert list(t["e2m1"]) == [g1[c] for c in range(16)]
+    assert list(t["e2m3"][:32]) == [g3[c] for c in range(32)]
+    import torch
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(t["e4m3"]), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(t["e4m3"][m], ref[m])
+    assert all(t["ue8m0"][b] == 2.0 ** (b - 127) for b in range(255))
+    assert oracle.bf16_value(0x3F80) == 1.0
+
+
+def _pin_packing():
+    for fmt_name, row, vals in read_packing_examples():
+        fmt = 1 if fmt_name == "e2m1" else 2
+        cols = 32 if fmt == 1 else 128
+        codes = np.zeros(oracle.code_row_bytes(fmt, cols), np.uint8)
+        codes[: len(row)] = np.frombuffer(row, np.uint8)
+        scales = np.full(oracle.scale_row_bytes(fmt, cols), 0x38 if fmt == 1 else 127, np.uint8)
+        assert list(oracle.decode(fmt, 1, cols, codes, scales)[0][: len(vals)]) == vals
+
+
+def _pin_scale_blocks():
+    cols = 64
+    codes = np.full((1, 32), 0x22, np.uint8)               # every weight 1.0
+    scales = np.array([[0x30, 0x38, 0x40, 0x48]], np.uint8)
+    W = oracle.decode(1, 1, cols, codes, scales)[0]
+    tab = oracle.tables()["e4m3"]
+    assert np.array_equal(W, np.repeat(tab[scales[0]], 16))
+
+
+def _pin_gemv():
+    rows, cols = 3, 256
+    codes = np.full((rows, cols // 2), 0x33, np.uint8)      # 1.5 everywhere
+    scales = np.full((rows, cols // 16), 0x30, np.uint8)    # 0.5
+    x = np.full((1, cols), 0x3F80, np.uint16)
+    assert (oracle.gemv(1, rows, cols, codes, scales, x) == cols * 0.75).all()
+
+
+def _rule(l, k):
+    key = lambda i: (1, 0.0, i) if np.isnan(l[i]) else (0, -float(l[i]), i)
+    return sorted(range(len(l)), key=key)[:k]
+
+
+def _pin_route():
+    import itertools
+    for pattern in itertools.product([0.0, 1.0], repeat=4):
+        l = np.array(pattern, np.float32)
+        for k in range(1, 5):
+            idx, w = oracle.route(l, k)
+            assert list(idx[0]) == _rule(l, k)
+            assert abs(w.sum() - 1) < 1e-15
+    l = np.array([np.nan, 1.0, np.nan, 1.0], np.float32)
+    assert list(oracle.route(l, 4)[0][0]) == [1, 3, 0, 2]
+    l = synth.router_logits(CFG)
+    idx, w = oracle.route(l, 3)
+    sel = np.take_along_axis(l.astype(np.float64), idx.astype(np.int64), axis=1)
+    assert np.allclose(w, softmax(sel, axis=1), rtol=1e-14, atol=0)
+
+
+def _pin_silu():
+    assert oracle.silu(0.0) == 0.0
+    for z in (-3.0, 0.7, 2.0):
+        assert abs(oracle.silu(z) - z * expit(z)) < 1e-15
+
+
+def _pin_ffn_and_layer():
+    H, I = CFG.hidden, CFG.inter
+    x = synth.hidden_states(CFG)
+    ex = {e: synth.expert_weights(CFG, e) for e in range(CFG.experts)}
+    sh = synth.expert_weights(CFG, CFG.experts)
+    l = synth.router_logits(CFG)
+    ys = {}
+    for e, ew in ex.items():
+        W13 = oracle.decode(1, 2 * I, H, ew["w13_codes"], ew["w13_scales"])
+        W2 = oracle.decode(1, H, I, ew["w2_codes"], ew["w2_scales"])
+        xf = np.array([oracle.bf16_value(int(b)) for b in x[0]])
+        g, u = W13[:I] @ xf, W13[I:] @ xf
+        ref = W2 @ (g * expit(g) * u)
+        y = oracle.ffn(1, H, I, ew, x[0])
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        ys[e] = y
+    _, _, out = oracle.layer(1, H, I, 4, 4, ex, x[:1], l[:1])
+    p = softmax(l[0].astype(np.float64))
+    ref = sum(p[e] * ys[e] for e in range(4))
+    assert np.allclose(out[0], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    _, _, a = oracle.layer(1, H, I, 4, 2, ex, x[:1], l[:1])
+    _, _, b = oracle.layer(1, H, I, 4, 2, ex, x[:1], l[:1], shared=sh, shared_inter=CFG.shared_inter)
+    ysh = oracle.ffn(1, H, CFG.shared_inter, sh, x[0])
+    assert np.allclose(b[0] - a[0], ysh, rtol=1e-12, atol=1e-12 * np.abs(ysh).max())
+
+
+PINS = [_pin_tables, _pin_packing, _pin_scale_blocks, _pin_gemv, _pin_route, _pin_silu, _pin_ffn_and_layer]
+
+
+def _failures():
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, KeyError) as exc:
+            failed.append(pin.__name__)
+    return failed
+
+
+def test_unmutated_oracle_passes_the_battery():
+    oracle.use_library(None)
+    assert _failures() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site must be unique: %s" % name
+    path = tmp_path / "oracle_mut.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("liboracle_%s.so" % name))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+                    "-ffp-contract=off", str(path), "-o", lib, "-lm"], check=True)
+    try:
+        oracle.use_library(lib)
+        failed = _failures()
+    finally:
+        oracle.use_library(None)
+    assert failed, "mutant %s passed every pin" % name
