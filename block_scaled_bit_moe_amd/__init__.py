@@ -1,0 +1,220 @@
+"""Python binding of the block-scaled low-bit MoE library (include/moeq.h).
+
+Argument marshalling only: torch tensors become device pointers and the
+current HIP stream; every step of the computation runs in the HIP kernels of
+libmoeq.so.  There is no fallback: if the library is not built, or a tensor is
+not on the GPU, the call raises.
+
+Functions carry the C names: moe_route_topk, moe_layer_workspace_bytes,
+moe_expert_ffn_q, moe_layer_decode, dense_gemv_q, moe_workspace_status,
+moe_last_error, moe_version.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmoeq.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EKERNEL = 0, -1, -2, -3, -4, -5
+MOE_FMT_E2M1_E4M3_B16, MOE_FMT_E2M3_UE8M0_B128 = 1, 2
+MOE_OUT_F32 = 1
+MOE_DECODER_LUT = 1 << 28
+MOE_DECODER_HW = 1 << 29
+MOE_DEBUG_SPIN_LIMIT = 1 << 30
+MAX_DECODE_TOKENS = 16
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__("moeq error %d: %s" % (code, message))
+        self.code = code
+
+
+class moe_qmat(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class moe_layer(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("w13_codes", ctypes.c_void_p), ("w13_scales", ctypes.c_void_p),
+                ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p),
+                ("sh13_codes", ctypes.c_void_p), ("sh13_scales", ctypes.c_void_p),
+                ("sh2_codes", ctypes.c_void_p), ("sh2_scales", ctypes.c_void_p)]
+
+
+def load_library(path=None):
+    """Load libmoeq.so (built in-tree by build.py).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError("libmoeq.so is not built (%s); run __graft_entry__.build()" % p)
+    lib = ctypes.CDLL(p)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer), i32, ctypes.POINTER(sz)]
+    lib.moe_expert_ffn_q.argtypes = [ctypes.POINTER(moe_layer), i32, vp, i32, vp, i32, vp, sz, vp]
+    lib.moe_layer_decode.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.dense_gemv_q.argtypes = [ctypes.POINTER(moe_qmat), vp, i32, vp, i32, vp]
+    lib.moe_workspace_status.argtypes = [vp, sz, vp]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_version.restype = i32
+    for f in ("moe_route_topk", "moe_layer_workspace_bytes", "moe_expert_ffn_q", "moe_layer_decode",
+              "dense_gemv_q", "moe_workspace_status"):
+        getattr(lib, f).restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def moe_last_error():
+    return load_library().moe_last_error().decode()
+
+
+def moe_version():
+    return load_library().moe_version()
+
+
+def _check(rc):
+    if rc != MOE_OK:
+        raise MoeError(rc, moe_last_error())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU (the library has no CPU path)" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
+
+
+class QMat:
+    """A block-scaled matrix [rows][cols] on the GPU (codes and scales uint8)."""
+
+    def __init__(self, fmt, rows, cols, codes, scales):
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+        self.codes, self.scales = codes, scales
+        self.c = moe_qmat(fmt, rows, cols, 0, _dev(codes, "codes", _U8).value, _dev(scales, "scales", _U8).value)
+
+
+class Layer:
+    """One MoE layer's weights on the GPU, as the moe_layer descriptor sees them.
+
+    w13_codes [E][2I][H*bits/8], w13_scales [E][2I][H/block], w2_codes [E][H][I*bits/8],
+    w2_scales [E][H][I/block]; optional shared_* arrays of the shared expert."""
+
+    def __init__(self, fmt, hidden, inter, n_experts, top_k, w13_codes, w13_scales, w2_codes, w2_scales,
+                 shared_inter=0, shared=None):
+        self.fmt, self.hidden, self.inter, self.n_experts, self.top_k = fmt, hidden, inter, n_experts, top_k
+        self.shared_inter = shared_inter
+        self.tensors = [w13_codes, w13_scales, w2_codes, w2_scales]
+        sh = [None] * 4
+        if shared_inter:
+            names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
+            sh = [_dev(shared[n], "shared " + n, _U8).value for n in names]
+            self.tensors += [shared[n] for n in names]
+        self.c = moe_layer(fmt, hidden, inter, n_experts, top_k, shared_inter,
+                           _dev(w13_codes, "w13_codes", _U8).value, _dev(w13_scales, "w13_scales", _U8).value,
+                           _dev(w2_codes, "w2_codes", _U8).value, _dev(w2_scales, "w2_scales", _U8).value,
+                           *sh)
+
+    def with_top_k(self, k):
+        """A descriptor of the same weights with another top-k."""
+        other = object.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+        c = moe_layer()
+        ctypes.pointer(c)[0] = self.c
+        c.top_k = k
+        other.c, other.top_k = c, k
+        return other
+
+
+def moe_route_topk(logits, k, idx=None, w=None):
+    """logits fp32 [T][E] -> (idx int32 [T][k], w fp32 [T][k])."""
+    T, E = logits.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(load_library().moe_route_topk(_dev(logits, "logits", (torch.float32,)), T, E, k,
+                                         _dev(idx, "idx", (torch.int32,)), _dev(w, "w", (torch.float32,)),
+                                         _stream()))
+    return idx, w
+
+
+def moe_layer_workspace_bytes(layer, T):
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_layer_workspace_bytes(ctypes.byref(layer.c), T, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(layer, T, device=None):
+    """A zeroed workspace of the size the call needs (torch memory)."""
+    return torch.zeros(moe_layer_workspace_bytes(layer, T), dtype=torch.uint8, device=device or "cuda")
+
+
+def _out(x, rows, cols, flags, out):
+    if out is not None:
+        return out
+    dt = torch.float32 if flags & MOE_OUT_F32 else torch.bfloat16
+    return torch.empty((rows, cols), dtype=dt, device=x.device)
+
+
+def moe_expert_ffn_q(layer, expert, x, y=None, flags=0, ws=None):
+    """One expert's SwiGLU FFN on the M rows of x (bf16 [M][H]); expert -1 = shared."""
+    M = x.shape[0]
+    y = _out(x, M, layer.hidden, flags, y)
+    ws = workspace(layer, M, x.device) if ws is None else ws
+    _check(load_library().moe_expert_ffn_q(ctypes.byref(layer.c), expert, _dev(x, "x", _BF16), M,
+                                           _dev(y, "y", (torch.bfloat16, torch.float32)), flags,
+                                           _dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return y
+
+
+def moe_layer_decode(layer, x, logits, out=None, idx_out=None, w_out=None, flags=0, ws=None):
+    """The MoE layer for the T rows of x: returns out [T][H] (bf16, or fp32 with MOE_OUT_F32)."""
+    T = x.shape[0]
+    out = _out(x, T, layer.hidden, flags, out)
+    ws = workspace(layer, T, x.device) if ws is None else ws
+    pi = _dev(idx_out, "idx_out", (torch.int32,)) if idx_out is not None else None
+    pw = _dev(w_out, "w_out", (torch.float32,)) if w_out is not None else None
+    _check(load_library().moe_layer_decode(ctypes.byref(layer.c), _dev(x, "x", _BF16),
+                                           _dev(logits, "logits", (torch.float32,)), T,
+                                           _dev(out, "out", (torch.bfloat16, torch.float32)), pi, pw, flags,
+                                           _dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return out
+
+
+def dense_gemv_q(W, x, y=None, flags=0):
+    """y [B][rows] = W x[b] for x bf16 [B][cols]."""
+    B = x.shape[0]
+    y = _out(x, B, W.rows, flags, y)
+    _check(load_library().dense_gemv_q(ctypes.byref(W.c), _dev(x, "x", _BF16), B,
+                                       _dev(y, "y", (torch.bfloat16, torch.float32)), flags, _stream()))
+    return y
+
+
+def moe_workspace_status(ws):
+    """MOE_OK, or raises MoeError(MOE_EKERNEL) when a kernel's bounded wait expired."""
+    _check(load_library().moe_workspace_status(_dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return MOE_OK

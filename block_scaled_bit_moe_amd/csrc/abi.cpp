@@ -1,0 +1,266 @@
+// abi.cpp -- the C ABI of include/moeq.h: argument validation (before anything
+// is enqueued), dispatch to the kernels, thread-local error text.
+// knivesysl README, introduction: the engine is one native library behind a C
+// ABI that Python loads; its "current benchmark" section: native errors name
+// the failing operation, not only a number.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/moeq.h"
+#include "kernels.h"
+
+using namespace moeq;
+
+static thread_local char g_err[512];
+
+static int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+static int ok() {
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+static bool al16(const void *p) { return p && (((uintptr_t)p) & 15u) == 0; }
+
+static int block_of(int fmt) { return fmt == MOE_FMT_E2M1_E4M3_B16 ? 32 : 128; }
+
+static int check_dim(const char *name, int v, int fmt) {
+    const int b = block_of(fmt);
+    if (v < b || v > MOE_MAX_DIM || v % b)
+        return fail(MOE_EINVAL, "%s=%d must be a multiple of %d in [%d, %d] for format %d", name, v, b, b,
+                    MOE_MAX_DIM, fmt);
+    return MOE_OK;
+}
+
+static int check_ptr(const char *name, const void *p) {
+    if (!p) return fail(MOE_EINVAL, "%s is NULL", name);
+    if (!al16(p)) return fail(MOE_EINVAL, "%s=%p is not 16-byte aligned", name, p);
+    return MOE_OK;
+}
+
+static int hip_fail(const char *op, hipError_t e) {
+    return fail(MOE_EHIP, "%s: %s (%d)", op, hipGetErrorString(e), (int)e);
+}
+
+static int decoder_from_flags(int flags) {
+    if (flags & MOE_DECODER_HW) return DEC_HW;
+    if (flags & MOE_DECODER_LUT) return DEC_LUT;
+    return decoder_choice();
+}
+
+int moeq::decoder_choice() {
+    static int choice = -1;
+    if (choice < 0) {
+        const char *v = getenv("MOEQ_DECODER");
+        choice = (v && !strcmp(v, "hw")) ? DEC_HW : DEC_LUT;
+    }
+    return choice;
+}
+
+#define CHECK(x)                         \
+    do {                                 \
+        int rc_ = (x);                   \
+        if (rc_ != MOE_OK) return rc_;   \
+    } while (0)
+
+static int validate_layer(const moe_layer *L) {
+    if (!L) return fail(MOE_EINVAL, "layer descriptor is NULL");
+    if (L->fmt != MOE_FMT_E2M1_E4M3_B16 && L->fmt != MOE_FMT_E2M3_UE8M0_B128)
+        return fail(MOE_EINVAL, "layer fmt=%d is not a known format", L->fmt);
+    CHECK(check_dim("hidden", L->hidden, L->fmt));
+    CHECK(check_dim("inter", L->inter, L->fmt));
+    if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_EINVAL, "n_experts=%d must be in [1, %d]", L->n_experts, MOE_MAX_EXPERTS);
+    const int kmax = L->n_experts < MOE_MAX_TOPK ? L->n_experts : MOE_MAX_TOPK;
+    if (L->top_k < 1 || L->top_k > kmax)
+        return fail(MOE_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)=%d]", L->top_k, MOE_MAX_TOPK, kmax);
+    if (L->shared_inter < 0) return fail(MOE_EINVAL, "shared_inter=%d is negative", L->shared_inter);
+    CHECK(check_ptr("w13_codes", L->w13_codes));
+    CHECK(check_ptr("w13_scales", L->w13_scales));
+    CHECK(check_ptr("w2_codes", L->w2_codes));
+    CHECK(check_ptr("w2_scales", L->w2_scales));
+    if (L->shared_inter > 0) {
+        CHECK(check_dim("shared_inter", L->shared_inter, L->fmt));
+        CHECK(check_ptr("sh13_codes", L->sh13_codes));
+        CHECK(check_ptr("sh13_scales", L->sh13_scales));
+        CHECK(check_ptr("sh2_codes", L->sh2_codes));
+        CHECK(check_ptr("sh2_scales", L->sh2_scales));
+    }
+    return MOE_OK;
+}
+
+static LayerArgs layer_args(const moe_layer *L) {
+    LayerArgs a;
+    a.w13c = (const uint8_t *)L->w13_codes;
+    a.w13s = (const uint8_t *)L->w13_scales;
+    a.w2c = (const uint8_t *)L->w2_codes;
+    a.w2s = (const uint8_t *)L->w2_scales;
+    a.sh13c = (const uint8_t *)L->sh13_codes;
+    a.sh13s = (const uint8_t *)L->sh13_scales;
+    a.sh2c = (const uint8_t *)L->sh2_codes;
+    a.sh2s = (const uint8_t *)L->sh2_scales;
+    a.fmt = L->fmt;
+    a.H = L->hidden;
+    a.I = L->inter;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.Ish = L->shared_inter;
+    return a;
+}
+
+static int decode_supported(const moe_layer *L, int T) {
+    if (T > DEC_MAX_T)
+        return fail(MOE_EUNSUPPORTED, "T=%d: more than %d tokens needs the prefill path, not in this build", T,
+                    DEC_MAX_T);
+    if (L->hidden > DEC_MAX_DIM || L->inter > DEC_MAX_DIM || L->shared_inter > DEC_MAX_DIM)
+        return fail(MOE_EUNSUPPORTED, "hidden/inter/shared_inter above %d are not supported by the decode kernels",
+                    DEC_MAX_DIM);
+    return MOE_OK;
+}
+
+static size_t ws_need(const moe_layer *L, int T) {
+    return decode_workspace_bytes(T, L->hidden, L->inter, L->shared_inter, L->top_k);
+}
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w, void *stream) {
+    CHECK(check_ptr("logits", logits));
+    CHECK(check_ptr("idx", idx));
+    CHECK(check_ptr("w", w));
+    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, MOE_MAX_EXPERTS);
+    const int kmax = E < MOE_MAX_TOPK ? E : MOE_MAX_TOPK;
+    if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k=%d must be in [1, min(E, %d)=%d]", k, MOE_MAX_TOPK, kmax);
+    hipError_t e = launch_route(logits, T, E, k, idx, w, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_route_topk launch", e);
+    return ok();
+}
+
+int moe_layer_workspace_bytes(const moe_layer *L, int T, size_t *bytes) {
+    if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+    CHECK(validate_layer(L));
+    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+    CHECK(decode_supported(L, T));
+    *bytes = ws_need(L, T);
+    return ok();
+}
+
+static int check_ws(const moe_layer *L, int T, const void *ws, size_t ws_bytes) {
+    if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws) & 255u) return fail(MOE_EWORKSPACE, "workspace %p is not 256-byte aligned", ws);
+    const size_t need = ws_need(L, T);
+    if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return MOE_OK;
+}
+
+int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void *y, int flags, void *ws,
+                     size_t ws_bytes, void *stream) {
+    CHECK(validate_layer(L));
+    if (expert < -1 || expert >= L->n_experts)
+        return fail(MOE_EINVAL, "expert=%d must be -1 (shared) or in [0, %d)", expert, L->n_experts);
+    if (expert == -1 && L->shared_inter <= 0) return fail(MOE_EINVAL, "expert=-1 but the layer has no shared expert");
+    if (M < 1 || M > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "M=%d must be in [1, %d]", M, MOE_MAX_TOKENS);
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("y", y));
+    CHECK(decode_supported(L, M));
+    CHECK(check_ws(L, M, ws, ws_bytes));
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.L = layer_args(L);
+    a.x = (const uint16_t *)x;
+    a.T = M;
+    a.out = y;
+    a.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+    a.mode = expert < 0 ? MODE_FIXED_SHARED : MODE_FIXED_ROUTED;
+    a.fixed_e = expert;
+    a.ws = (uint8_t *)ws;
+    a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    hipError_t e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_expert_ffn_q launch", e);
+    return ok();
+}
+
+int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int T, void *out, int32_t *idx_out,
+                     float *w_out, int flags, void *ws, size_t ws_bytes, void *stream) {
+    CHECK(validate_layer(L));
+    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("logits", logits));
+    CHECK(check_ptr("out", out));
+    if (idx_out && !al16(idx_out)) return fail(MOE_EINVAL, "idx_out is not 16-byte aligned");
+    if (w_out && !al16(w_out)) return fail(MOE_EINVAL, "w_out is not 16-byte aligned");
+    CHECK(decode_supported(L, T));
+    CHECK(check_ws(L, T, ws, ws_bytes));
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.L = layer_args(L);
+    a.x = (const uint16_t *)x;
+    a.logits = logits;
+    a.T = T;
+    a.out = out;
+    a.idx_out = idx_out;
+    a.w_out = w_out;
+    a.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+    a.mode = MODE_ROUTE;
+    a.fixed_e = 0;
+    a.ws = (uint8_t *)ws;
+    a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    hipError_t e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_layer_decode launch", e);
+    return ok();
+}
+
+int dense_gemv_q(const moe_qmat *W, const void *x, int B, void *y, int flags, void *stream) {
+    if (!W) return fail(MOE_EINVAL, "matrix descriptor is NULL");
+    if (W->fmt != MOE_FMT_E2M1_E4M3_B16 && W->fmt != MOE_FMT_E2M3_UE8M0_B128)
+        return fail(MOE_EINVAL, "matrix fmt=%d is not a known format", W->fmt);
+    if (W->reserved != 0) return fail(MOE_EINVAL, "matrix reserved field must be 0");
+    if (W->rows < 1 || W->rows > (1 << 24)) return fail(MOE_EINVAL, "rows=%d must be in [1, %d]", W->rows, 1 << 24);
+    CHECK(check_dim("cols", W->cols, W->fmt));
+    if (W->cols > DEC_MAX_DIM)
+        return fail(MOE_EUNSUPPORTED, "cols=%d above %d is not supported by the GEMV kernel", W->cols, DEC_MAX_DIM);
+    if (B < 1 || B > MOE_MAX_GEMV_BATCH) return fail(MOE_EINVAL, "B=%d must be in [1, %d]", B, MOE_MAX_GEMV_BATCH);
+    CHECK(check_ptr("codes", W->codes));
+    CHECK(check_ptr("scales", W->scales));
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("y", y));
+    hipError_t e = launch_gemv(W->fmt, decoder_from_flags(flags), (const uint8_t *)W->codes,
+                               (const uint8_t *)W->scales, W->rows, W->cols, (const uint16_t *)x, B, y,
+                               (flags & MOE_OUT_F32) ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("dense_gemv_q launch", e);
+    return ok();
+}
+
+int moe_workspace_status(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if (ws_bytes < WS_HEADER) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs at least %zu", ws_bytes,
+                                          (size_t)WS_HEADER);
+    uint32_t err = 0;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(&err, ws, sizeof err, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail("moe_workspace_status read", e);
+    if (err) {
+        e = hipMemsetAsync(ws, 0, sizeof err, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail("moe_workspace_status clear", e);
+        return fail(MOE_EKERNEL, "a kernel's bounded inter-workgroup wait expired; its output is invalid");
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,319 @@
+// common.h -- device building blocks shared by the gfx950 kernels.
+//
+// Formats (knivesysl README, "formats"; colibri README, "DeepSeek V4"):
+//   FMT 1: e2m1 codes, two per byte (low nibble = even element), one fp8 e4m3
+//          scale per 16 weights;
+//   FMT 2: e2m3 codes as a little-endian 6-bit stream, one UE8M0 scale per 128.
+// Everything here works on "units" of 32 consecutive weights of one row:
+//   e2m1: 16 code bytes + 2 scale bytes (blocks 2u and 2u+1)
+//   e2m3: 24 code bytes + the scale byte of block u/4
+// A unit decodes to 16 bf16x2 registers (exact: every e2m1/e2m3 value has at
+// most 4 significant bits) which v_dot2c_f32_bf16 multiplies with 16 bf16x2 of
+// the activation, accumulating in fp32; the block scale is applied once per
+// block with an fp32 FMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace moeq {
+
+typedef uint32_t u32;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(6))) u32 u32x6_t;
+typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32_t;
+
+constexpr int FMT_E2M1 = 1;
+constexpr int FMT_E2M3 = 2;
+constexpr int WAVE = 64;
+
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<FMT_E2M1> {
+    static constexpr int UNIT_CODE_BYTES = 16;
+    static constexpr int BLOCK = 16;
+    __host__ __device__ static inline int64_t code_row_bytes(int64_t cols) { return cols / 2; }
+    __host__ __device__ static inline int64_t scale_row_bytes(int64_t cols) { return cols / 16; }
+};
+template <> struct Fmt<FMT_E2M3> {
+    static constexpr int UNIT_CODE_BYTES = 24;
+    static constexpr int BLOCK = 128;
+    __host__ __device__ static inline int64_t code_row_bytes(int64_t cols) { return cols * 3 / 4; }
+    __host__ __device__ static inline int64_t scale_row_bytes(int64_t cols) { return cols / 128; }
+};
+
+// ----------------------------------------------------------------------------
+// Value tables, built on the device from the bit fields.
+// A minifloat with `eb` exponent bits of bias `bias`, `mb` mantissa bits,
+// subnormals at exponent field 0: the float value of code c (sign at bit eb+mb).
+__device__ __host__ inline float minifloat_value(u32 c, int eb, int mb, int bias) {
+    u32 m = c & ((1u << mb) - 1u);
+    u32 e = (c >> mb) & ((1u << eb) - 1u);
+    u32 s = (c >> (mb + eb)) & 1u;
+    float mag = (e == 0) ? ldexpf((float)m / (float)(1u << mb), 1 - bias)
+                         : ldexpf(1.0f + (float)m / (float)(1u << mb), (int)e - bias);
+    return s ? -mag : mag;
+}
+
+__device__ inline u32 bf16_bits_exact(float f) {   // f has <= 8 significant bits
+    return __builtin_bit_cast(u32, f) >> 16;
+}
+
+// LDS table sizes (in u32 entries)
+constexpr int LUT_E2M1_PAIR = 256;     // byte -> bf16x2 (low nibble in the low half)
+constexpr int LUT_E2M3_PAIR = 4096;    // 12 bits (two codes) -> bf16x2
+constexpr int LUT_SCALE = 256;         // e4m3 or UE8M0 byte -> fp32
+
+struct Luts {
+    u32 *pair;      // e2m1 or e2m3 pair table
+    float *scale;   // e4m3 or UE8M0
+};
+
+// Fill the tables (call by the whole block, then __syncthreads()).
+template <int FMT>
+__device__ inline void build_luts(const Luts &L, int tid, int nthreads, bool need_pair) {
+    if (FMT == FMT_E2M1) {
+        if (need_pair)
+            for (int b = tid; b < LUT_E2M1_PAIR; b += nthreads) {
+                u32 lo = bf16_bits_exact(minifloat_value(b & 15, 2, 1, 1));
+                u32 hi = bf16_bits_exact(minifloat_value(b >> 4, 2, 1, 1));
+                L.pair[b] = lo | (hi << 16);
+            }
+        for (int b = tid; b < LUT_SCALE; b += nthreads)
+            L.scale[b] = ((b & 0x7F) == 0x7F) ? __builtin_nanf("") : minifloat_value(b, 4, 3, 7);
+    } else {
+        if (need_pair)
+            for (int p = tid; p < LUT_E2M3_PAIR; p += nthreads) {
+                u32 lo = bf16_bits_exact(minifloat_value(p & 63, 2, 3, 1));
+                u32 hi = bf16_bits_exact(minifloat_value(p >> 6, 2, 3, 1));
+                L.pair[p] = lo | (hi << 16);
+            }
+        for (int b = tid; b < LUT_SCALE; b += nthreads)
+            L.scale[b] = (b == 255) ? __builtin_nanf("") : ldexpf(1.0f, b - 127);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Raw unit loads
+template <int FMT> struct Unit;
+template <> struct Unit<FMT_E2M1> {
+    uint4 c;        // 16 code bytes = 32 weights
+    u32 s;          // two e4m3 scale bytes in bits 0..15
+};
+template <> struct Unit<FMT_E2M3> {
+    uint2 c0, c1, c2;   // 24 code bytes = 32 weights
+    u32 s;              // the UE8M0 scale byte of this unit's block
+};
+
+__device__ inline uint4 ldg16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ inline uint2 ldg8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+
+// Load unit u of a row (codes/scales point at the row's first byte).
+template <int FMT>
+__device__ inline void load_unit(Unit<FMT> &U, const uint8_t *codes, const uint8_t *scales, int u) {
+    if constexpr (FMT == FMT_E2M1) {
+        U.c = ldg16(codes + (int64_t)u * 16);
+        U.s = *reinterpret_cast<const uint16_t *>(scales + 2 * u);
+    } else {
+        const uint8_t *p = codes + (int64_t)u * 24;
+        U.c0 = ldg8(p);
+        U.c1 = ldg8(p + 8);
+        U.c2 = ldg8(p + 16);
+        U.s = scales[u >> 2];
+    }
+}
+
+// Decode a unit into 16 bf16x2 words (pair i = weights 2i, 2i+1; low half = even).
+template <int FMT, int DEC>
+__device__ inline void decode_unit(const Unit<FMT> &U, const Luts &L, u32 w[16]) {
+    if constexpr (FMT == FMT_E2M1) {
+        const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
+        if constexpr (DEC == DEC_HW) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[4 * i + 0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 0));
+                w[4 * i + 1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 1));
+                w[4 * i + 2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 2));
+                w[4 * i + 3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 3));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) w[4 * i + b] = L.pair[(d[i] >> (8 * b)) & 0xFF];
+            }
+        }
+    } else {
+        const u32 d[6] = {U.c0.x, U.c0.y, U.c1.x, U.c1.y, U.c2.x, U.c2.y};
+        if constexpr (DEC == DEC_HW) {
+            u32x6_t v;
+            v[0] = d[0]; v[1] = d[1]; v[2] = d[2]; v[3] = d[3]; v[4] = d[4]; v[5] = d[5];
+            bf16x32_t r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(v, 1.0f);
+            typedef __attribute__((ext_vector_type(16))) u32 u32x16_t;
+            u32x16_t rr = __builtin_bit_cast(u32x16_t, r);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = rr[i];
+        } else {
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const int bit = 12 * p, dw = bit >> 5, off = bit & 31;
+                u32 f;
+                if (off + 12 <= 32) f = (d[dw] >> off) & 0xFFFu;
+                else f = __builtin_amdgcn_alignbit(d[dw + 1], d[dw], off) & 0xFFFu;
+                w[p] = L.pair[f];
+            }
+        }
+    }
+}
+
+__device__ inline float dot2(u32 a, u32 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// acc += dot(unit weights, x) with the block scale(s) applied once per block.
+template <int FMT>
+__device__ inline float unit_dot(const u32 w[16], const u32 x[16], float s0, float s1, float acc) {
+    if constexpr (FMT == FMT_E2M1) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p0 = dot2(w[i], x[i], p0);
+#pragma unroll
+        for (int i = 8; i < 16; ++i) p1 = dot2(w[i], x[i], p1);
+        acc = __builtin_fmaf(s0, p0, acc);
+        return __builtin_fmaf(s1, p1, acc);
+    } else {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = dot2(w[i], x[i], p);
+        (void)s1;
+        return __builtin_fmaf(s0, p, acc);
+    }
+}
+
+// Same with the activation carried as bf16 hi + lo (x = hi + lo to ~16 bits):
+// both parts meet the same decoded weights and the same block scale.
+template <int FMT>
+__device__ inline float unit_dot_split(const u32 w[16], const u32 xh[16], const u32 xl[16], float s0, float s1,
+                                       float acc) {
+    if constexpr (FMT == FMT_E2M1) {
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { p0 = dot2(w[i], xh[i], p0); p0 = dot2(w[i], xl[i], p0); }
+#pragma unroll
+        for (int i = 8; i < 16; ++i) { p1 = dot2(w[i], xh[i], p1); p1 = dot2(w[i], xl[i], p1); }
+        acc = __builtin_fmaf(s0, p0, acc);
+        return __builtin_fmaf(s1, p1, acc);
+    } else {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { p = dot2(w[i], xh[i], p); p = dot2(w[i], xl[i], p); }
+        (void)s1;
+        return __builtin_fmaf(s0, p, acc);
+    }
+}
+
+template <int FMT>
+__device__ inline void unit_scales(const Unit<FMT> &U, const Luts &L, float &s0, float &s1) {
+    if constexpr (FMT == FMT_E2M1) {
+        s0 = L.scale[U.s & 0xFF];
+        s1 = L.scale[(U.s >> 8) & 0xFF];
+    } else {
+        s0 = L.scale[U.s & 0xFF];
+        s1 = 0.f;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Wave reductions.  Sum over groups of G consecutive lanes (G a power of two
+// <= 64); every lane of the group ends with the group's sum, formed by the same
+// butterfly in every group, so the order is fixed.
+template <int G>
+__device__ inline float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+
+// ----------------------------------------------------------------------------
+// Routing helpers.  Order key of an fp32 logit: larger float -> larger key,
+// +0 and -0 equal, NaN below every number.  The 64-bit composite appends the
+// complement of the expert index so equal keys rank the lower index first.
+__device__ inline u32 logit_key(float f) {
+    u32 b = __builtin_bit_cast(u32, f);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0u;   // NaN
+    if (b == 0x80000000u) b = 0u;                      // -0 == +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline uint64_t rank_key(float f, int e) {
+    return ((uint64_t)logit_key(f) << 32) | (uint64_t)(~(u32)e);
+}
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
+    u32 lo = (u32)v, hi = (u32)(v >> 32);
+    lo = __shfl_xor(lo, m, WAVE);
+    hi = __shfl_xor(hi, m, WAVE);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < WAVE; m <<= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+constexpr int ROUTE_MAX_PER_LANE = 16;   // E <= 1024
+
+// One wave routes one token: the k best experts in rank order and their
+// softmax weights over the k picks (Strata docs/INTEL.md, "The engine itself on
+// Intel": router_top10, for any k).  Lane 0 .. k-1 end with (idx, w) of rank
+// lane; other lanes return idx -1.
+template <int PER_LANE>
+__device__ inline void route_one_token_wave(const float *__restrict__ logits, int E, int k, int lane,
+                                            int &my_idx, float &my_w) {
+    uint64_t key[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+        int e = j * WAVE + lane;
+        key[j] = (e < E) ? rank_key(logits[e], e) : 0ull;
+    }
+    my_idx = -1;
+    float my_l = 0.f;
+    float l0 = 0.f;
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) best = key[j] > best ? key[j] : best;
+        uint64_t win = wave_max_u64(best);
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) key[j] = (key[j] == win) ? 0ull : key[j];
+        int e = (int)(~(u32)win);
+        // the winner's logit, recovered from its key (exact inverse of logit_key)
+        u32 kk = (u32)(win >> 32);
+        u32 b = (kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk;
+        float lv = (kk == 0u) ? __builtin_nanf("") : __builtin_bit_cast(float, b);
+        if (r == 0) l0 = lv;
+        if (lane == r) { my_idx = e; my_l = lv; }
+    }
+    // weights: exp(l_r - l_0) / sum over the k picks (fp32, fixed order r = 0..k-1)
+    float ex = (lane < k) ? expf(my_l - l0) : 0.f;
+    float z = 0.f;
+    for (int r = 0; r < k; ++r) z += __shfl(ex, r, WAVE);
+    my_w = (lane < k) ? ex / z : 0.f;
+}
+
+__device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    u32 u = __builtin_bit_cast(u32, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace moeq

@@ -1,0 +1,7 @@
+// decode_e2m1_hw.hip -- one (format, decoder) instantiation set of the
+// single-launch MoE decode kernel (decode_impl.h), compiled on its own.
+#include "decode_impl.h"
+
+namespace moeq {
+hipError_t decode_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s) { return decode_fd<FMT_E2M1, DEC_HW>(a, s); }
+}  // namespace moeq

@@ -1,0 +1,60 @@
+// kernels.h -- launchers of the gfx950 kernels (host side of each .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq {
+
+// Decoder choice: LUT = tables in LDS indexed by whole bytes / 12-bit code
+// pairs; HW = gfx950's scaled fp4/fp6 -> bf16 conversion instructions.  Both
+// are exact; which is faster is measured.
+constexpr int DEC_LUT = 0;
+constexpr int DEC_HW = 1;
+
+struct LayerArgs {
+    const uint8_t *w13c, *w13s, *w2c, *w2s;       // routed experts, stacked
+    const uint8_t *sh13c, *sh13s, *sh2c, *sh2s;   // shared expert (Ish > 0)
+    int fmt, H, I, E, k, Ish;
+};
+
+enum { MODE_ROUTE = 0, MODE_FIXED_ROUTED = 1, MODE_FIXED_SHARED = 2 };
+
+struct DecodeArgs {
+    LayerArgs L;
+    const uint16_t *x;        // bf16 [T][H]
+    const float *logits;      // fp32 [T][E]  (MODE_ROUTE)
+    int T;
+    void *out;                // [T][H] bf16 or fp32
+    int32_t *idx_out;         // nullable
+    float *w_out;             // nullable
+    int out_f32;
+    int mode, fixed_e;
+    uint8_t *ws;
+    uint32_t spin_limit;
+};
+
+// decode-path workspace: header (counters, error word) + h (hi/lo bf16) + y partials
+constexpr size_t WS_HEADER = 16384;
+constexpr int WS_ERR = 0;          // u32 offsets into the header
+constexpr int WS_EXIT = 1;
+constexpr int WS_GU = 16;          // gu_done[<= 1024]
+constexpr int WS_DN = 16 + 1024;   // dn_done[<= 3072]
+constexpr int DEC_MAX_T = 16;
+constexpr int DEC_MAX_GROUPS = DEC_MAX_T * 32 + 1;
+constexpr int DEC_MAX_PAIRS = DEC_MAX_T * 33;
+constexpr int DEC_MAX_DIM = 8192;  // H, I, Ish on the decode path (x/h held in registers)
+constexpr int DEC_S1 = 16;         // I-rows (gate and up) per gate/up item
+constexpr int DEC_S2 = 64;         // output rows per down item
+
+size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k);
+
+hipError_t launch_route(const float *logits, int T, int E, int k, int32_t *idx, float *w, hipStream_t s);
+hipError_t launch_gemv(int fmt, int dec, const uint8_t *codes, const uint8_t *scales, int rows, int cols,
+                       const uint16_t *x, int B, void *y, int out_f32, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s);
+
+int decoder_choice();    // DEC_LUT or DEC_HW (MOEQ_DECODER=lut|hw, read once)
+
+}  // namespace moeq

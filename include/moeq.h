@@ -93,6 +93,10 @@ enum {
 /* Flags. */
 enum {
     MOE_OUT_F32 = 1,        /* write the output as fp32 (the value before bf16 rounding) */
+    MOE_DECODER_LUT = 1 << 28,  /* decode codes through byte-indexed tables in LDS */
+    MOE_DECODER_HW = 1 << 29,   /* decode codes with gfx950's fp4/fp6 -> bf16 conversions
+                                   (both decoders are exact and give identical results; with
+                                   neither flag the library default is used) */
     MOE_DEBUG_SPIN_LIMIT = 1 << 30  /* test hook: inter-workgroup waits give up almost at once,
                                        so the MOE_EKERNEL path can be exercised; output invalid */
 };

@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, and rejects bad arguments before touching the GPU (every call here
+fails validation, so no HIP work is attempted)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_bit_moe_amd as moeq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+FAKE = 0x10000          # an aligned non-null address; never dereferenced by validation
+FAKE2 = 0x20000
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+|dense_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moeq.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"moe_route_topk", "moe_layer_workspace_bytes", "moe_expert_ffn_q", "moe_layer_decode",
+                          "dense_gemv_q", "moe_last_error", "moe_version", "moe_workspace_status"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.moe_version() >= 100
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def _layer(**kw):
+    d = dict(fmt=1, hidden=256, inter=512, n_experts=8, top_k=2, shared_inter=0,
+             w13_codes=FAKE, w13_scales=FAKE, w2_codes=FAKE, w2_scales=FAKE)
+    d.update(kw)
+    L = moeq.moe_layer()
+    for k, v in d.items():
+        setattr(L, k, v)
+    return L
+
+
+def test_route_validation(lib):
+    assert lib.moe_route_topk(None, 1, 8, 2, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert "logits" in _err(lib)
+    assert lib.moe_route_topk(FAKE + 4, 1, 8, 2, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert "aligned" in _err(lib)
+    assert lib.moe_route_topk(FAKE, 0, 8, 2, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert lib.moe_route_topk(FAKE, 1, 8, 9, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert "k=9" in _err(lib)
+    assert lib.moe_route_topk(FAKE, 1, 1025, 2, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert lib.moe_route_topk(FAKE, 1, 64, 33, FAKE, FAKE, None) == moeq.MOE_EINVAL
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("fmt", 3, "fmt"), ("hidden", 48, "hidden"), ("inter", 0, "inter"), ("n_experts", 0, "n_experts"),
+    ("top_k", 9, "top_k"), ("top_k", 0, "top_k"), ("shared_inter", -32, "shared_inter"),
+    ("w13_codes", 0, "w13_codes"), ("w2_scales", FAKE + 8, "w2_scales"), ("shared_inter", 48, "shared_inter"),
+])
+def test_layer_validation(lib, field, value, needle):
+    L = _layer(**{field: value})
+    n = ctypes.c_size_t(0)
+    rc = lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n))
+    assert rc == moeq.MOE_EINVAL and needle in _err(lib)
+    assert n.value == 0
+
+
+def test_e2m3_dims_must_be_whole_blocks(lib):
+    L = _layer(fmt=2, hidden=256, inter=512 + 32)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_EINVAL
+    assert "multiple of 128" in _err(lib)
+
+
+def test_shared_pointers_required(lib):
+    L = _layer(shared_inter=512)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_EINVAL
+    assert "sh13_codes" in _err(lib)
+
+
+def test_workspace_bytes_and_checks(lib):
+    L = _layer()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_OK
+    need = n.value
+    assert need > 16384
+    # too small, misaligned, NULL: workspace errors, nothing launched
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 1, FAKE, None, None, 0, FAKE2, need - 1,
+                                None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 1, FAKE, None, None, 0, FAKE2 + 16, need,
+                                None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 1, FAKE, None, None, 0, None, need,
+                                None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, None, 1, FAKE, None, None, 0, FAKE2, need,
+                                None) == moeq.MOE_EINVAL
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 1, FAKE, FAKE + 4, None, 0, FAKE2, need,
+                                None) == moeq.MOE_EINVAL
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 0, FAKE, None, None, 0, FAKE2, need,
+                                None) == moeq.MOE_EINVAL
+
+
+def test_expert_ffn_validation(lib):
+    L = _layer()
+    n = ctypes.c_size_t(0)
+    lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n))
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), 8, FAKE, 1, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), -1, FAKE, 1, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
+    assert "shared" in _err(lib)
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), 0, FAKE, 0, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
+
+
+def test_gemv_validation(lib):
+    W = moeq.moe_qmat(2, 100, 5120, 0, FAKE, FAKE)
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 0, FAKE, 0, None) == moeq.MOE_EINVAL
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 9, FAKE, 0, None) == moeq.MOE_EINVAL
+    W.cols = 5000
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 1, FAKE, 0, None) == moeq.MOE_EINVAL
+    W.cols, W.reserved = 5120, 1
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 1, FAKE, 0, None) == moeq.MOE_EINVAL
+    W.reserved, W.fmt = 0, 0
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 1, FAKE, 0, None) == moeq.MOE_EINVAL
+    W.fmt, W.codes = 2, 0
+    assert lib.dense_gemv_q(ctypes.byref(W), FAKE, 1, FAKE, 0, None) == moeq.MOE_EINVAL
+    assert lib.dense_gemv_q(None, FAKE, 1, FAKE, 0, None) == moeq.MOE_EINVAL
+
+
+def test_status_validation(lib):
+    assert lib.moe_workspace_status(None, 1 << 20, None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_workspace_status(FAKE, 100, None) == moeq.MOE_EWORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    logits = torch.zeros(1, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        moeq.moe_route_topk(logits, 2)
