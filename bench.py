@@ -1,0 +1,272 @@
+"""Benchmark of the MoE decode layer on one MI355X.
+
+A step is one call of moe_layer_decode on one batch of synthetic input: route,
+group by expert, gate | up, SiLU-multiply, down, combine -- the whole hot path.
+Inputs are resident in HBM before the timed region starts.  To defeat the
+256 MB last-level cache, the layer is replicated R times and every step uses
+the next replica and a fresh set of router logits (so it selects different
+experts).  The K timed steps are captured once in a HIP graph and replayed, so
+the figure is GPU time, not Python launch overhead; the eager figure is
+reported beside it.
+
+Prints one JSON line.  --config picks another workload (toy_decode,
+dense_gemv_e2m3, wide_decode, batched_decode, prefill).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "wide_decode"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default=DEFAULT_CONFIG)
+    p.add_argument("--batch", type=int, default=1, help="GEMV tokens (dense_gemv_e2m3 only)")
+    p.add_argument("--replicas", type=int, default=0, help="weight replicas (0: enough for >= 4x the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    p.add_argument("--profile-steps", type=int, default=0,
+                   help="only run this many eager steps after warmup (for rocprofv3 counter runs)")
+    return p.parse_args()
+
+
+def bytes_per_expert(cfg, inter):
+    import synth
+    f = cfg.fmt
+    H = cfg.hidden
+    return (2 * inter * (synth.code_row_bytes(f, H) + synth.scale_row_bytes(f, H))
+            + H * (synth.code_row_bytes(f, inter) + synth.scale_row_bytes(f, inter)))
+
+
+def topk_sets(logits, k):
+    """Distinct experts selected per call (bookkeeping for the byte count)."""
+    order = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]
+    return np.unique(order)
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.torch.cuda.synchronize()
+        self.e0.record()
+
+    def stop(self):
+        self.e1.record()
+        self.torch.cuda.synchronize()
+        return self.e0.elapsed_time(self.e1) * 1e-3      # seconds
+
+
+def run_steps(torch, calls, steps, warmup, eager):
+    """Time `steps` calls (cycling through `calls`) after `warmup` untimed ones."""
+    n = len(calls)
+    for i in range(warmup):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    seq = [calls[(warmup + i) % n] for i in range(steps)]
+    t = Timer(torch)
+    if eager:
+        t.start()
+        for c in seq:
+            c()
+        return t.stop(), "eager"
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for c in seq:
+                c()
+    torch.cuda.synchronize()
+    g.replay()                      # one untimed replay
+    t.start()
+    g.replay()
+    return t.stop(), "hipgraph"
+
+
+def cpu_baseline_moe(cfg, seconds, logits_list, x):
+    """The oracle on the host cores, call after call of the same workload, until
+    ~`seconds` of oracle time.  Generating the selected experts' bytes on the
+    host is not timed.  Returns (calls, oracle seconds)."""
+    import oracle
+    import synth
+    cache = {}
+    sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
+    spent, done = 0.0, 0
+    while done < len(logits_list) and spent < seconds:
+        l = logits_list[done]
+        idx, _ = oracle.route(l, cfg.top_k)
+        ex = {}
+        for e in np.unique(idx):
+            e = int(e)
+            if e not in cache:
+                cache[e] = synth.expert_weights(cfg, e)
+            ex[e] = cache[e]
+        t1 = time.perf_counter()
+        oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, x, l, shared=sh,
+                     shared_inter=cfg.shared_inter)
+        spent += time.perf_counter() - t1
+        done += 1
+    return done, spent
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(expert sharding over RCCL is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_bit_moe_amd as moeq
+    import synth
+    from synth import configs
+    from synth.device import dev_bf16, dev_u8, upload_layer_tensors
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moeq.load_library()
+    cfg = configs.ALL[a.config]
+    cores = len(os.sched_getaffinity(0))
+    omp = int(os.environ.get("OMP_NUM_THREADS", cores))
+    result = {}
+
+    if isinstance(cfg, configs.GemvConfig):
+        B = a.batch
+        c, s = synth.gemv_weights(cfg)
+        wbytes = c.nbytes + s.nbytes
+        R = a.replicas or max(1, -(-(1 << 30) // wbytes))
+        Ws = []
+        base_c, base_s = dev_u8(c), dev_u8(s)
+        for r in range(R):
+            cc, ss = (base_c, base_s) if r == 0 else (base_c.clone(), base_s.clone())
+            Ws.append(moeq.QMat(cfg.fmt, cfg.rows, cfg.cols, cc, ss))
+        x = dev_bf16(synth.gemv_x(cfg, B))
+        y = torch.empty((B, cfg.rows), dtype=torch.bfloat16, device="cuda")
+        calls = [(lambda W=W: moeq.dense_gemv_q(W, x, y=y)) for W in Ws]
+        if a.profile_steps:
+            for i in range(a.warmup + a.profile_steps):
+                calls[i % len(calls)]()
+            torch.cuda.synchronize()
+            return
+        secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
+        per = secs / a.steps
+        tokens_per_s = B / per
+        achieved = wbytes / per / 1e9
+        metric_value = tokens_per_s
+        workload = {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols, "batch": B, "fmt": "e2m3+ue8m0/128",
+                    "replicas": R}
+        kernel = "gemv_kernel"
+        cpu = None
+        if not a.no_cpu_baseline:
+            import oracle
+            n_rows = 256
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < a.cpu_seconds:
+                oracle.gemv(cfg.fmt, cfg.rows, cfg.cols, c, s, synth.gemv_x(cfg, B), row_list=np.arange(n_rows) + reps)
+                reps += 1
+            el = time.perf_counter() - t0
+            frac = reps * n_rows / cfg.rows
+            cpu = {"value": B * frac / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
+                   "sample": "%d row blocks of %d rows (%.4f of the matrix) x B=%d, scaled to whole GEMVs" %
+                             (reps, n_rows, frac, B),
+                   "weight_GBps": frac * wbytes / el / 1e9}
+    else:
+        T = cfg.tokens
+        if T > moeq.MAX_DECODE_TOKENS:
+            print("config %s needs the prefill path" % cfg.name, file=sys.stderr)
+        per_expert = bytes_per_expert(cfg, cfg.inter)
+        layer_bytes = cfg.experts * per_expert
+        R = a.replicas or max(1, min(32, -(-(4 << 30) // layer_bytes)))
+        devs, shared = upload_layer_tensors(cfg)
+        L0 = moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, devs["w13_codes"],
+                        devs["w13_scales"], devs["w2_codes"], devs["w2_scales"],
+                        shared_inter=cfg.shared_inter, shared=shared)
+        layers = [L0]
+        for r in range(1, R):
+            t = [tt.clone() for tt in L0.tensors[:4]]
+            sh = None
+            if cfg.shared_inter:
+                sh = dict(zip(("w13_codes", "w13_scales", "w2_codes", "w2_scales"), [tt.clone() for tt in L0.tensors[4:]]))
+            layers.append(moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, *t,
+                                     shared_inter=cfg.shared_inter, shared=sh))
+        NL = 64
+        logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
+        logits = [torch.from_numpy(l).cuda() for l in logits_host]
+        xh = synth.hidden_states(cfg)
+        x = dev_bf16(xh)
+        ws = moeq.workspace(L0, T)
+        out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        n = max(R, NL)
+        calls = [(lambda i=i: moeq.moe_layer_decode(layers[i % R], x, logits[i % NL], out=out, ws=ws))
+                 for i in range(n)]
+        if a.profile_steps:
+            for i in range(a.warmup + a.profile_steps):
+                calls[i % len(calls)]()
+            torch.cuda.synchronize()
+            moeq.moe_workspace_status(ws)
+            return
+        secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
+        moeq.moe_workspace_status(ws)
+        per = secs / a.steps
+        # algorithmic bytes: the packed codes + scales of every expert the call uses, read once
+        used = [len(topk_sets(logits_host[(a.warmup + i) % NL], cfg.top_k)) + (1 if cfg.shared_inter else 0)
+                for i in range(a.steps)]
+        wbytes = float(np.mean(used)) * per_expert if not cfg.shared_inter else \
+            float(np.mean([u - 1 for u in used])) * per_expert + bytes_per_expert(cfg, cfg.shared_inter)
+        tokens_per_s = T / per
+        achieved = wbytes / per / 1e9
+        metric_value = tokens_per_s
+        workload = {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "experts": cfg.experts,
+                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
+                    "fmt": "e2m1+e4m3/16", "replicas": R, "logit_sets": NL,
+                    "experts_read_per_call": float(np.mean(used))}
+        kernel = "decode_kernel"
+        cpu = None
+        if not a.no_cpu_baseline:
+            done, el = cpu_baseline_moe(cfg, a.cpu_seconds, logits_host, xh)
+            cpu = {"value": done * T / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
+                   "sample": "%d call(s) of the same workload (%d token(s) each, fresh logits); %.1f s of "
+                             "oracle time" % (done, T, el)}
+
+    line = {
+        "metric": "MoE decode layer tokens/s and effective weight GB/s (% of 8 TB/s HBM)",
+        "value": metric_value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": per * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generator; random-init weights of the workload's shapes)",
+        "config": dict(workload, launch=mode),
+        "effective_weight_GBps": achieved,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,22 +173,31 @@ __device__ inline float dot2(u32 a, u32 b, float c) {
 }
 
 // acc += dot(unit weights, x) with the block scale(s) applied once per block.
+// Two interleaved partial sums per block keep the dot2 dependency chains short.
 template <int FMT>
 __device__ inline float unit_dot(const u32 w[16], const u32 x[16], float s0, float s1, float acc) {
     if constexpr (FMT == FMT_E2M1) {
-        float p0 = 0.f, p1 = 0.f;
+        float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p0 = dot2(w[i], x[i], p0);
-#pragma unroll
-        for (int i = 8; i < 16; ++i) p1 = dot2(w[i], x[i], p1);
-        acc = __builtin_fmaf(s0, p0, acc);
-        return __builtin_fmaf(s1, p1, acc);
+        for (int i = 0; i < 8; i += 2) {
+            a0 = dot2(w[i], x[i], a0);
+            b0 = dot2(w[i + 1], x[i + 1], b0);
+            a1 = dot2(w[8 + i], x[8 + i], a1);
+            b1 = dot2(w[9 + i], x[9 + i], b1);
+        }
+        acc = __builtin_fmaf(s0, a0 + b0, acc);
+        return __builtin_fmaf(s1, a1 + b1, acc);
     } else {
-        float p = 0.f;
+        float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p = dot2(w[i], x[i], p);
+        for (int i = 0; i < 16; i += 4) {
+            a = dot2(w[i], x[i], a);
+            b = dot2(w[i + 1], x[i + 1], b);
+            c = dot2(w[i + 2], x[i + 2], c);
+            d = dot2(w[i + 3], x[i + 3], d);
+        }
         (void)s1;
-        return __builtin_fmaf(s0, p, acc);
+        return __builtin_fmaf(s0, (a + b) + (c + d), acc);
     }
 }
 
@@ -198,19 +207,27 @@ template <int FMT>
 __device__ inline float unit_dot_split(const u32 w[16], const u32 xh[16], const u32 xl[16], float s0, float s1,
                                        float acc) {
     if constexpr (FMT == FMT_E2M1) {
-        float p0 = 0.f, p1 = 0.f;
+        float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { p0 = dot2(w[i], xh[i], p0); p0 = dot2(w[i], xl[i], p0); }
-#pragma unroll
-        for (int i = 8; i < 16; ++i) { p1 = dot2(w[i], xh[i], p1); p1 = dot2(w[i], xl[i], p1); }
-        acc = __builtin_fmaf(s0, p0, acc);
-        return __builtin_fmaf(s1, p1, acc);
+        for (int i = 0; i < 8; ++i) {
+            a0 = dot2(w[i], xh[i], a0);
+            b0 = dot2(w[i], xl[i], b0);
+            a1 = dot2(w[8 + i], xh[8 + i], a1);
+            b1 = dot2(w[8 + i], xl[8 + i], b1);
+        }
+        acc = __builtin_fmaf(s0, a0 + b0, acc);
+        return __builtin_fmaf(s1, a1 + b1, acc);
     } else {
-        float p = 0.f;
+        float a = 0.f, b = 0.f, c = 0.f, d = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { p = dot2(w[i], xh[i], p); p = dot2(w[i], xl[i], p); }
+        for (int i = 0; i < 16; i += 2) {
+            a = dot2(w[i], xh[i], a);
+            b = dot2(w[i], xl[i], b);
+            c = dot2(w[i + 1], xh[i + 1], c);
+            d = dot2(w[i + 1], xl[i + 1], d);
+        }
         (void)s1;
-        return __builtin_fmaf(s0, p, acc);
+        return __builtin_fmaf(s0, (a + b) + (c + d), acc);
     }
 }
 
@@ -226,13 +243,34 @@ __device__ inline void unit_scales(const Unit<FMT> &U, const Luts &L, float &s0,
 }
 
 // ----------------------------------------------------------------------------
-// Wave reductions.  Sum over groups of G consecutive lanes (G a power of two
-// <= 64); every lane of the group ends with the group's sum, formed by the same
-// butterfly in every group, so the order is fixed.
-template <int G>
-__device__ inline float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, WAVE);
+// Wave reductions with DPP (no LDS traffic, a few cycles per step).  Sum over
+// aligned groups of G lanes; the same butterfly runs in every group, so the
+// order of the additions is fixed.  For G <= 16 every lane of the group holds
+// the sum; for G = 32 / 64 the sum is valid in the group's first lane only
+// (the rows of 16 are added there in ascending order with readlane).
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float group_sum_dpp(float v, int G) {
+    if (G >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (G >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (G >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+    if (G >= 16) v += dpp_mov<0x140>(v);  // row_mirror
+    if (G == 32) {
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+        v = ((threadIdx.x & 63) < 32) ? r0 + r1 : r2 + r3;
+    } else if (G == 64) {
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+        v = ((r0 + r1) + r2) + r3;
+    }
     return v;
 }
 

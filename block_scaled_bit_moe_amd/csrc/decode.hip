@@ -13,7 +13,7 @@ size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
     (void)T;
     (void)k;
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
-    return WS_HEADER + 2 * (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint16_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float);
+    return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint32_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {

@@ -34,11 +34,54 @@
 
 namespace moeq {
 
+// Inter-workgroup traffic.  Data that one workgroup writes and another reads
+// inside the launch (h and the fp32 partials) moves with device-coherent
+// (sc1) stores and loads, so no L2 write-back or invalidate is ever needed;
+// a writer waits for its stores to complete (s_waitcnt vmcnt(0)) before it
+// bumps a relaxed counter, and a reader issues its loads only after it has
+// seen the count.
 __device__ inline u32 ld_relaxed_agent(const u32 *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline void st_relaxed_agent(u32 *p, u32 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline u32 add_release_agent(u32 *p, u32 v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline u32 add_acqrel_agent(u32 *p, u32 v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ inline u32 add_relaxed_agent(u32 *p, u32 v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((ext_vector_type(4))) u32 u32x4_t;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, u32 bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset `off`, read at device coherence (sc1)
+__device__ inline u32x4_t ld16_coherent(__amdgpu_buffer_rsrc_t r, u32 off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16);
+}
+
+// h of one (token, expert) pair is stored as 32-bit words, unit by unit: the
+// 32 elements of unit u occupy words [32u, 32u+32): first 16 words hold the
+// bf16 "hi" parts of element pairs (2i, 2i+1), the next 16 the "lo" parts
+// (h = hi + lo to about 16 significant bits).
+template <int Q, int MT>
+__device__ inline void load_h_units(u32 (&xh)[Q][MT][16], u32 (&xl)[Q][MT][16], __amdgpu_buffer_rsrc_t r,
+                                    const int (&pos)[MT], int Imax, int U, int lr, int LPR) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int u = lr + LPR * q;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (u < U && pos[t] >= 0) {
+                const u32 base = (u32)((pos[t] * Imax + 32 * u) * 4);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    u32x4_t a = ld16_coherent(r, base + 16 * v);
+                    xh[q][t][4 * v + 0] = a.x; xh[q][t][4 * v + 1] = a.y; xh[q][t][4 * v + 2] = a.z; xh[q][t][4 * v + 3] = a.w;
+                    u32x4_t b = ld16_coherent(r, base + 64 + 16 * v);
+                    xl[q][t][4 * v + 0] = b.x; xl[q][t][4 * v + 1] = b.y; xl[q][t][4 * v + 2] = b.z; xl[q][t][4 * v + 3] = b.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) { xh[q][t][i] = 0u; xl[q][t][i] = 0u; }
+            }
+        }
+    }
+}
 
 template <int MT>
 struct DecShared {
@@ -105,9 +148,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int T = a.T, H = ly.H, I = ly.I, E = ly.E, Ish = ly.Ish;
     const int Imax = I > Ish ? I : Ish;
     u32 *hdr = reinterpret_cast<u32 *>(a.ws);
-    uint16_t *h_hi = reinterpret_cast<uint16_t *>(a.ws + WS_HEADER);
-    uint16_t *h_lo = h_hi + (size_t)DEC_MAX_PAIRS * Imax;
-    float *ybuf = reinterpret_cast<float *>(h_lo + (size_t)DEC_MAX_PAIRS * Imax);
+    u32 *hl = reinterpret_cast<u32 *>(a.ws + WS_HEADER);                 // [pairs][Imax] words
+    u32 *ybuf = hl + (size_t)DEC_MAX_PAIRS * Imax;                         // [pairs][H] fp32 bits
+    const __amdgpu_buffer_rsrc_t hl_rsrc = make_rsrc(hl, (u32)((size_t)DEC_MAX_PAIRS * Imax * 4));
 
     build_luts<FMT>(L, tid, 256, DEC == DEC_LUT);
 
@@ -251,23 +294,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                             for (int j = 0; j < MT; ++j) S.gu[vr[b]][j] = acc[b][j];
                 }
                 __syncthreads();
-                for (int q = tid; q < DEC_S1 * MT; q += 256) {
-                    const int i = q / MT, j = q % MT;
+                for (int q = tid; q < (DEC_S1 / 2) * MT; q += 256) {
+                    const int kp = q / MT, j = q % MT;
                     if (tt + j < mg) {
-                        const float gg = S.gu[i][j], uu = S.gu[DEC_S1 + i][j];
-                        const float h = silu_f32(gg) * uu;
-                        const uint16_t hi = f32_to_bf16_rne(h);
-                        const float rest = h - __builtin_bit_cast(float, (u32)hi << 16);
-                        const size_t o = (size_t)(pos0 + tt + j) * Imax + s * DEC_S1 + i;
-                        h_hi[o] = hi;
-                        h_lo[o] = f32_to_bf16_rne(rest);
+                        const int i0 = 2 * kp;
+                        const float h0 = silu_f32(S.gu[i0][j]) * S.gu[DEC_S1 + i0][j];
+                        const float h1 = silu_f32(S.gu[i0 + 1][j]) * S.gu[DEC_S1 + i0 + 1][j];
+                        const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
+                        const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
+                        const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
+                        const int p = (s * DEC_S1 + i0) >> 1, uu = p >> 4, kk2 = p & 15;
+                        u32 *row = hl + (size_t)(pos0 + tt + j) * Imax + 32 * uu;
+                        st_relaxed_agent(row + kk2, hi0 | (hi1 << 16));
+                        st_relaxed_agent(row + 16 + kk2, lo0 | (lo1 << 16));
                     }
                 }
                 __syncthreads();
             }
-            __threadfence();
+            wait_stores();
             __syncthreads();
-            if (tid == 0) add_release_agent(&gu_done[g], 1u);
+            if (tid == 0) add_relaxed_agent(&gu_done[g], 1u);
         } else {
             // ------------------------------------------------ down projection partials
             const int d = item - n_gu;
@@ -284,7 +330,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 }
             }
             __syncthreads();
-            fence_acquire_agent();
             const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
             const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)e * H * crbI : ly.sh2c;
             const uint8_t *s2 = (e >= 0) ? ly.w2s + (int64_t)e * H * srbI : ly.sh2s;
@@ -294,15 +339,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const int o_lo = j * DEC_S2, o_hi = (o_lo + DEC_S2 < H) ? o_lo + DEC_S2 : H;
             for (int tt = 0; tt < mg; tt += MT) {
                 u32 xh[QD][MT][16], xl[QD][MT][16];
-                const uint16_t *hp[MT], *lp[MT];
+                int pp[MT];
 #pragma unroll
-                for (int jj = 0; jj < MT; ++jj) {
-                    const bool ok = tt + jj < mg;
-                    hp[jj] = ok ? h_hi + (size_t)(pos0 + tt + jj) * Imax : nullptr;
-                    lp[jj] = ok ? h_lo + (size_t)(pos0 + tt + jj) * Imax : nullptr;
-                }
-                load_x_units<QD, MT>(xh, hp, UI, lrd, LPRd);
-                load_x_units<QD, MT>(xl, lp, UI, lrd, LPRd);
+                for (int jj = 0; jj < MT; ++jj) pp[jj] = (tt + jj < mg) ? pos0 + tt + jj : -1;
+                load_h_units<QD, MT>(xh, xl, hl_rsrc, pp, Imax, UI, lrd, LPRd);
                 constexpr int R = 2;
                 for (int o0 = o_lo + wv * RPWd; o0 < o_hi; o0 += 4 * RPWd * R) {
                     const uint8_t *crow[R], *srow[R];
@@ -321,23 +361,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                         if (orow[b] < o_hi && lrd == 0)
 #pragma unroll
                             for (int jj = 0; jj < MT; ++jj)
-                                if (tt + jj < mg) ybuf[(size_t)(pos0 + tt + jj) * H + orow[b]] = acc[b][jj];
+                                if (tt + jj < mg)
+                                    st_relaxed_agent(ybuf + (size_t)(pos0 + tt + jj) * H + orow[b],
+                                                     __builtin_bit_cast(u32, acc[b][jj]));
                 }
             }
-            __threadfence();
+            wait_stores();
             __syncthreads();
-            if (tid == 0) S.flag = (add_acqrel_agent(&dn_done[j], 1u) == (u32)(NG - 1));
+            if (tid == 0) S.flag = (add_relaxed_agent(&dn_done[j], 1u) == (u32)(NG - 1));
             __syncthreads();
             if (S.flag) {
                 // ------------------------------------------------ combine this row slice
-                fence_acquire_agent();
                 const int width = o_hi - o_lo;
                 for (int q = tid; q < T * width; q += 256) {
                     const int t = q / width, o = o_lo + q % width;
                     float acc = 0.f;
                     for (int r = 0; r < kk; ++r)
-                        acc = __builtin_fmaf(S.w[t * kk + r], ybuf[(size_t)S.pos_of[t][r] * H + o], acc);
-                    if (add_shared) acc += ybuf[(size_t)S.pos_of[t][kk] * H + o];
+                        acc = __builtin_fmaf(S.w[t * kk + r],
+                                             __builtin_bit_cast(float, ld_relaxed_agent(ybuf + (size_t)S.pos_of[t][r] * H + o)),
+                                             acc);
+                    if (add_shared) acc += __builtin_bit_cast(float, ld_relaxed_agent(ybuf + (size_t)S.pos_of[t][kk] * H + o));
                     const int64_t oi = (int64_t)t * H + o;
                     if (a.out_f32) reinterpret_cast<float *>(a.out)[oi] = acc;
                     else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16_rne(acc);
@@ -348,9 +391,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 
     // ---------------------------------------------------------- exit: the last workgroup resets
+    wait_stores();
     __syncthreads();
     if (tid == 0) {
-        const u32 old = add_acqrel_agent(&hdr[WS_EXIT], 1u);
+        const u32 old = add_relaxed_agent(&hdr[WS_EXIT], 1u);
         if (old == gridDim.x - 1) {
             for (int g = 0; g < NG; ++g) st_relaxed_agent(&gu_done[g], 0u);
             for (int j = 0; j < n_slices; ++j) st_relaxed_agent(&dn_done[j], 0u);

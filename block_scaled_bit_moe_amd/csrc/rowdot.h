@@ -5,7 +5,8 @@
 // lane's units sit in registers for the whole pass (they are the same for
 // every row).  R rows are loaded before any is decoded so that R * Q unit
 // loads per lane are in flight.  The lane partial sums are combined by a
-// butterfly over the LPR lanes, identical for every row and every token.
+// DPP butterfly over the LPR lanes, identical for every row and every token;
+// the sum is valid in the first lane of each row's lane group.
 #pragma once
 
 #include "common.h"
@@ -79,8 +80,7 @@ __device__ inline void rows_dot(const uint8_t *const (&crow)[R], const uint8_t *
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-            for (int m = 1; m < LPR; m <<= 1) acc[b][t] += __shfl_xor(acc[b][t], m, WAVE);
+        for (int t = 0; t < MT; ++t) acc[b][t] = group_sum_dpp(acc[b][t], LPR);
 }
 
 // Lanes per row for a row of U units: the largest power of two <= min(64, U).
