@@ -275,71 +275,95 @@ __device__ inline float group_sum_dpp(float v, int G) {
 }
 
 // ----------------------------------------------------------------------------
-// Routing helpers.  Order key of an fp32 logit: larger float -> larger key,
-// +0 and -0 equal, NaN below every number.  The 64-bit composite appends the
-// complement of the expert index so equal keys rank the lower index first.
+// Routing helpers.  Order key of an fp32 logit: a larger float gets a larger
+// key, +0 and -0 get the same key, NaN gets 1 (below every number) and 0 marks
+// an entry already taken.
 __device__ inline u32 logit_key(float f) {
     u32 b = __builtin_bit_cast(u32, f);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0u;   // NaN
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 1u;   // NaN
     if (b == 0x80000000u) b = 0u;                      // -0 == +0
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline uint64_t rank_key(float f, int e) {
-    return ((uint64_t)logit_key(f) << 32) | (uint64_t)(~(u32)e);
+__device__ inline float logit_of_key(u32 k) {
+    if (k <= 1u) return __builtin_nanf("");
+    const u32 b = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __builtin_bit_cast(float, b);
 }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
-    u32 lo = (u32)v, hi = (u32)(v >> 32);
-    lo = __shfl_xor(lo, m, WAVE);
-    hi = __shfl_xor(hi, m, WAVE);
-    return ((uint64_t)hi << 32) | lo;
+template <int CTRL, int ROWMASK = 0xF>
+__device__ inline u32 dpp_u32(u32 old, u32 v) {
+    return (u32)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, false);
 }
 
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 1; m < WAVE; m <<= 1) {
-        uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+// max (or min) over the 64 lanes, returned uniform
+__device__ inline u32 wave_max_u32(u32 v) {
+    v = max(v, dpp_u32<0xB1>(v, v));          // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E>(v, v));          // quad_perm [2,3,0,1]
+    v = max(v, dpp_u32<0x141>(v, v));         // row_half_mirror
+    v = max(v, dpp_u32<0x140>(v, v));         // row_mirror
+    v = max(v, dpp_u32<0x142, 0xA>(v, v));    // row_bcast:15 into rows 1, 3
+    v = max(v, dpp_u32<0x143, 0xC>(v, v));    // row_bcast:31 into rows 2, 3
+    return (u32)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-constexpr int ROUTE_MAX_PER_LANE = 16;   // E <= 1024
+__device__ inline u32 wave_min_u32(u32 v) {
+    v = min(v, dpp_u32<0xB1>(v, v));
+    v = min(v, dpp_u32<0x4E>(v, v));
+    v = min(v, dpp_u32<0x141>(v, v));
+    v = min(v, dpp_u32<0x140>(v, v));
+    v = min(v, dpp_u32<0x142, 0xA>(v, v));
+    v = min(v, dpp_u32<0x143, 0xC>(v, v));
+    return (u32)__builtin_amdgcn_readlane((int)v, 63);
+}
 
 // One wave routes one token: the k best experts in rank order and their
 // softmax weights over the k picks (Strata docs/INTEL.md, "The engine itself on
-// Intel": router_top10, for any k).  Lane 0 .. k-1 end with (idx, w) of rank
-// lane; other lanes return idx -1.
+// Intel": router_top10, for any k).  Expert e sits in lane e % 64, slot e / 64,
+// so among equal keys the lowest slot and then the lowest lane is the lowest
+// index.  Each of the k rounds takes the wave maximum of the lanes' best keys
+// (DPP); a single lane holding it wins outright (the usual case), otherwise the
+// lowest index among the holders is found with a wave minimum.  Lanes
+// 0 .. k-1 end with (idx, w) of rank = lane; other lanes return idx -1.
 template <int PER_LANE>
 __device__ inline void route_one_token_wave(const float *__restrict__ logits, int E, int k, int lane,
                                             int &my_idx, float &my_w) {
-    uint64_t key[PER_LANE];
+    u32 key[PER_LANE];
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
-        int e = j * WAVE + lane;
-        key[j] = (e < E) ? rank_key(logits[e], e) : 0ull;
+        const int e = j * WAVE + lane;
+        key[j] = (e < E) ? logit_key(logits[e]) : 0u;
     }
     my_idx = -1;
-    float my_l = 0.f;
-    float l0 = 0.f;
+    float my_l = 0.f, l0 = 0.f;
     for (int r = 0; r < k; ++r) {
-        uint64_t best = 0ull;
+        // lane's best key and the lowest slot holding it
+        u32 best = key[0];
+        int bj = 0;
 #pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) best = key[j] > best ? key[j] : best;
-        uint64_t win = wave_max_u64(best);
+        for (int j = 1; j < PER_LANE; ++j) {
+            const bool gt = key[j] > best;
+            best = gt ? key[j] : best;
+            bj = gt ? j : bj;
+        }
+        const u32 m = wave_max_u32(best);
+        const uint64_t holders = __ballot(best == m);
+        int e;
+        if (__popcll(holders) == 1) {
+            const int wl = __ffsll((long long)holders) - 1;
+            e = __builtin_amdgcn_readlane(bj, wl) * WAVE + wl;
+        } else {
+            e = (int)wave_min_u32(best == m ? (u32)(bj * WAVE + lane) : 0xFFFFFFFFu);
+        }
+        const int wj = e / WAVE, wl = e % WAVE;
 #pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) key[j] = (key[j] == win) ? 0ull : key[j];
-        int e = (int)(~(u32)win);
-        // the winner's logit, recovered from its key (exact inverse of logit_key)
-        u32 kk = (u32)(win >> 32);
-        u32 b = (kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk;
-        float lv = (kk == 0u) ? __builtin_nanf("") : __builtin_bit_cast(float, b);
+        for (int j = 0; j < PER_LANE; ++j) key[j] = (lane == wl && j == wj) ? 0u : key[j];
+        const float lv = logit_of_key(m);
         if (r == 0) l0 = lv;
         if (lane == r) { my_idx = e; my_l = lv; }
     }
     // weights: exp(l_r - l_0) / sum over the k picks (fp32, fixed order r = 0..k-1)
-    float ex = (lane < k) ? expf(my_l - l0) : 0.f;
+    const float ex = (lane < k) ? expf(my_l - l0) : 0.f;
     float z = 0.f;
     for (int r = 0; r < k; ++r) z += __shfl(ex, r, WAVE);
     my_w = (lane < k) ? ex / z : 0.f;

@@ -1,5 +1,7 @@
 // decode.hip -- host side of the single-launch MoE decode: workspace size and
 // dispatch to the (format, decoder) instantiations.
+#include <stdlib.h>
+
 #include "kernels.h"
 
 namespace moeq {
@@ -8,15 +10,39 @@ hipError_t decode_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
 hipError_t decode_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
 hipError_t decode_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
 hipError_t decode_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
+hipError_t decode1_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
+hipError_t decode1_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
+hipError_t decode1_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
+hipError_t decode1_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
+
+// MOEQ_DECODE1=0 routes single-token calls to the general kernel (for A/B
+// measurement; both give identical results).
+static bool single_token_kernel_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char *v = getenv("MOEQ_DECODE1");
+        on = (v && v[0] == '0') ? 0 : 1;
+    }
+    return on == 1;
+}
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
     (void)T;
     (void)k;
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
-    return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint32_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float);
+    // header | h words of the general kernel | its fp32 partials | tagged h of the single-token kernel
+    return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint32_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float) +
+           (size_t)33 * Imax * sizeof(uint64_t);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {
+    if (a.T == 1 && a.mode == MODE_ROUTE && single_token_kernel_enabled()) {
+        hipError_t e;
+        if (a.L.fmt == 1) e = dec == DEC_HW ? decode1_launch_e2m1_hw(a, s) : decode1_launch_e2m1_lut(a, s);
+        else e = dec == DEC_HW ? decode1_launch_e2m3_hw(a, s) : decode1_launch_e2m3_lut(a, s);
+        if (e != hipErrorNotSupported) return e;
+        (void)hipGetLastError();
+    }
     if (a.L.fmt == 1) return dec == DEC_HW ? decode_launch_e2m1_hw(a, s) : decode_launch_e2m1_lut(a, s);
     return dec == DEC_HW ? decode_launch_e2m3_hw(a, s) : decode_launch_e2m3_lut(a, s);
 }

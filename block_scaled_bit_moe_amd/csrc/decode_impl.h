@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
             const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)e * H * crbI : ly.sh2c;
             const uint8_t *s2 = (e >= 0) ? ly.w2s + (int64_t)e * H * srbI : ly.sh2s;
-            const int UI = Ig / 32, LPRd = lanes_per_row(UI), RPWd = WAVE / LPRd;
+            const int UI = Ig / 32, LPRd = down_lanes_per_row(I, Ish), RPWd = WAVE / LPRd;
             const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
             const int mg = S.g_count[g], pos0 = S.g_start[g];
             const int o_lo = j * DEC_S2, o_hi = (o_lo + DEC_S2 < H) ? o_lo + DEC_S2 : H;
@@ -455,12 +455,8 @@ hipError_t decode_fd(const DecodeArgs &a, hipStream_t s) {
     const int UH = L.H / 32, QG = (UH + lanes_per_row(UH) - 1) / lanes_per_row(UH);
     const int Imax = L.I > L.Ish ? L.I : L.Ish;
     // QD must cover both the routed and the shared intermediate size
-    int QD = 1;
-    for (int Iv : {L.I, L.Ish}) {
-        if (Iv <= 0) continue;
-        const int U = Iv / 32, q = (U + lanes_per_row(U) - 1) / lanes_per_row(U);
-        if (q > QD) QD = q;
-    }
+    const int LPRd = down_lanes_per_row(L.I, L.Ish);
+    const int QD = ((Imax / 32) + LPRd - 1) / LPRd;
     (void)Imax;
     const int MT = (a.T == 1) ? 1 : 2;
     switch (QG) {

@@ -1,15 +1,135 @@
 // gemv.hip -- dense_gemv_q: y[b] = W x[b] for a block-scaled W and B <= 8 bf16
 // tokens that share every decoded weight (knivesysl README, "formats": the fp6
 // e2m3 projections with a power-of-two scale per 128; Strata docs/INTEL.md,
-// "Decode round 2": aligned 16-byte weight loads).  Bandwidth-bound: each
-// weight byte is read once from HBM per pass of MT tokens.
+// "Decode round 2": aligned 16-byte weight loads, codebook lookups kept off the
+// critical path).
+//
+// Bandwidth-bound: every weight byte is read from HBM once per pass of MT
+// tokens.  For several tokens each workgroup streams a contiguous range of row
+// chunks through an LDS ring (stream.h): the x registers of 4 tokens leave no
+// room for deep register pipelines.  One workgroup per CU (the ring takes most
+// of the LDS), chunks split evenly over the workgroups.  For one token the
+// register-pipelined kernel below is faster (measured: 25.5 vs 39.6 us on the
+// 25600 x 5120 e2m3 matrix).
 #include "kernels.h"
 #include "rowdot.h"
+#include "stream.h"
 
 namespace moeq {
 
+constexpr int GEMV_L = 7;    // 16-byte loads per thread per chunk: 28 KiB stages
+constexpr int GEMV_NS = 4;   // stages in flight
+
+template <int FMT, int DEC, int Q, int MT>
+__global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restrict__ codes,
+                                                   const uint8_t *__restrict__ scales, int rows, int cols,
+                                                   const uint16_t *__restrict__ x, int B, void *__restrict__ y,
+                                                   int out_f32, int RC, int cpw) {
+    constexpr int L_ = GEMV_L, NS = GEMV_NS, STAGE = L_ * 4096;
+    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * STAGE];
+    __shared__ u32 s_pair[PAIR];
+    __shared__ float s_scale[LUT_SCALE];
+    const Luts Lt{s_pair, s_scale};
+    const int tid = threadIdx.x;
+    build_luts<FMT>(Lt, tid, 256, DEC == DEC_LUT);
+    __syncthreads();
+
+    const int crb = (int)Fmt<FMT>::code_row_bytes(cols), srb = (int)Fmt<FMT>::scale_row_bytes(cols);
+    const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
+    const int lane = tid & 63, w = tid >> 6, lr = lane & (LPR - 1), rsub = lane / LPR;
+    const __amdgpu_buffer_rsrc_t rc = rsrc_of(codes, (uint64_t)rows * crb);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(scales, (uint64_t)rows * srb);
+    const int NC = (rows + RC - 1) / RC;
+    const int c0 = blockIdx.x * cpw;
+    const int n = (c0 + cpw < NC ? c0 + cpw : NC) - c0;
+    if (n <= 0) return;   // uniform over the workgroup
+
+    for (int t0 = 0; t0 < B; t0 += MT) {
+        u32 xr[Q][MT][16];
+        const uint16_t *xp[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xp[t] = (t0 + t < B) ? x + (int64_t)(t0 + t) * cols : nullptr;
+        load_x_units<Q, MT>(xr, xp, U, lr, LPR);
+
+        auto src = [&](int i) {
+            const int r0 = (c0 + i) * RC;
+            const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
+            return chunk_src(rc, rs, r0, nr, (u32)crb, (u32)srb);
+        };
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < n) issue_chunk<L_>(ring + i * STAGE, src(i), tid);
+
+        for (int i = 0; i < n; ++i) {
+            if (i + NS - 1 < n) {
+                issue_chunk<L_>(ring + ((i + NS - 1) % NS) * STAGE, src(i + NS - 1), tid);
+                wait_vm<(NS - 1) * L_>();
+            } else {
+                wait_vm<0>();
+            }
+            __syncthreads();
+            const int r0 = (c0 + i) * RC;
+            const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
+            const uint8_t *sc = ring + (i % NS) * STAGE;
+            const uint8_t *ss = sc + ((nr * crb + 1023) / 1024) * 1024 + ((r0 * srb) & 15);
+            constexpr int R = 2;
+            for (int base = w * RPW; base < nr; base += RING_WAVES * RPW * R) {
+                int row[R];
+#pragma unroll
+                for (int b = 0; b < R; ++b) {
+                    const int rr = base + b * RING_WAVES * RPW + rsub;
+                    row[b] = rr < nr ? rr : -1;
+                }
+                float acc[R][MT];
+                rows_dot_lds<FMT, DEC, Q, MT, R, false>(sc, ss, row, crb, srb, U, lr, LPR, xr, xr, Lt, acc);
+#pragma unroll
+                for (int b = 0; b < R; ++b) {
+                    if (row[b] < 0 || lr != 0) continue;
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        if (t0 + t >= B) continue;
+                        const int64_t o = (int64_t)(t0 + t) * rows + r0 + row[b];
+                        if (out_f32) reinterpret_cast<float *>(y)[o] = acc[b][t];
+                        else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(acc[b][t]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+static int num_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (cus <= 0) cus = 1;
+    }
+    return cus;
+}
+
+template <int FMT, int DEC, int Q, int MT>
+static hipError_t gemv_ring_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
+                          void *y, int out_f32, hipStream_t s) {
+    const int crb = (int)Fmt<FMT>::code_row_bytes(cols), srb = (int)Fmt<FMT>::scale_row_bytes(cols);
+    const int RC = rows_per_chunk(GEMV_L, crb, srb);
+    const int NC = (rows + RC - 1) / RC;
+    const int G0 = num_cus();
+    const int cpw = (NC + G0 - 1) / G0;
+    const int G = (NC + cpw - 1) / cpw;
+    hipLaunchKernelGGL((gemv_ring_kernel<FMT, DEC, Q, MT>), dim3(G), dim3(256), 0, s, codes, scales, rows, cols, x, B, y,
+                       out_f32, RC, cpw);
+    return hipGetLastError();
+}
+
+// Register-pipelined variant: the x units stay in VGPRs and every wave keeps
+// R rows of loads in flight.  Used for one token, where it streams faster
+// than the ring (fewer VGPRs for x, more waves per CU).
 template <int FMT, int DEC, int Q, int MT, int R>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ codes,
+__global__ __launch_bounds__(256) void gemv_reg_kernel(const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, int rows, int cols,
                                                    const uint16_t *__restrict__ x, int B, void *__restrict__ y,
                                                    int out_f32) {
@@ -66,14 +186,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t *__restrict__ c
 }
 
 template <int FMT, int DEC, int Q, int MT>
-static hipError_t gemv_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
+static hipError_t gemv_reg_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
                           void *y, int out_f32, hipStream_t s) {
     constexpr int R = 2;
     const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
     const int ngroups = (rows + RPW - 1) / RPW;
     int blocks = (ngroups + 4 * R - 1) / (4 * R);
     if (blocks > 256 * 16) blocks = 256 * 16;
-    hipLaunchKernelGGL((gemv_kernel<FMT, DEC, Q, MT, R>), dim3(blocks), dim3(256), 0, s, codes, scales, rows, cols, x,
+    hipLaunchKernelGGL((gemv_reg_kernel<FMT, DEC, Q, MT, R>), dim3(blocks), dim3(256), 0, s, codes, scales, rows, cols, x,
                        B, y, out_f32);
     return hipGetLastError();
 }
@@ -85,8 +205,8 @@ static hipError_t gemv_q(const uint8_t *codes, const uint8_t *scales, int rows, 
     const bool one = (B == 1);
 #define GO(QQ)                                                                                    \
     if (Q == QQ) {                                                                                \
-        if (one) return gemv_go<FMT, DEC, QQ, 1>(codes, scales, rows, cols, x, B, y, out_f32, s); \
-        return gemv_go<FMT, DEC, QQ, 4>(codes, scales, rows, cols, x, B, y, out_f32, s);          \
+        if (one) return gemv_reg_go<FMT, DEC, QQ, 1>(codes, scales, rows, cols, x, B, y, out_f32, s); \
+        return gemv_ring_go<FMT, DEC, QQ, 4>(codes, scales, rows, cols, x, B, y, out_f32, s);         \
     }
     GO(1) GO(2) GO(3) GO(4)
 #undef GO

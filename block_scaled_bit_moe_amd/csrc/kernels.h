@@ -39,6 +39,8 @@ struct DecodeArgs {
 constexpr size_t WS_HEADER = 16384;
 constexpr int WS_ERR = 0;          // u32 offsets into the header
 constexpr int WS_EXIT = 1;
+constexpr int WS_ARRIVE = 2;
+constexpr int WS_EPOCH = 3;       // single-token kernel: calls completed on this workspace
 constexpr int WS_GU = 16;          // gu_done[<= 1024]
 constexpr int WS_DN = 16 + 1024;   // dn_done[<= 3072]
 constexpr int DEC_MAX_T = 16;
@@ -49,6 +51,16 @@ constexpr int DEC_S1 = 16;         // I-rows (gate and up) per gate/up item
 constexpr int DEC_S2 = 64;         // output rows per down item
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k);
+
+// Lanes per row of the down projection: one mapping for every expert of the
+// layer (set by the smaller intermediate size), so a token's arithmetic does
+// not depend on which kernel or which other tokens share the call.
+__host__ __device__ inline int down_lanes_per_row(int I, int Ish) {
+    const int m = (Ish > 0 && Ish < I) ? Ish : I;
+    int U = m / 32, l = 64;
+    while (l > U && l > 1) l >>= 1;
+    return l;
+}
 
 hipError_t launch_route(const float *logits, int T, int E, int k, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_gemv(int fmt, int dec, const uint8_t *codes, const uint8_t *scales, int rows, int cols,

@@ -54,6 +54,9 @@
  *    nothing was enqueued, outputs are untouched, and moe_last_error() returns
  *    text naming the argument and the rule it broke (thread-local).
  *  - Device pointers must be 16-byte aligned; workspaces 256-byte aligned.
+ *    Code and scale arrays are read in 16-byte pieces: when an array's length
+ *    is not a multiple of 16, the bytes up to the end of its last 16-byte
+ *    granule may be read (and ignored); they never lie outside that granule.
  *  - Arithmetic: weights are decoded exactly, products and sums are formed in
  *    fp32, the SiLU and the softmax in fp32, and the output is rounded to bf16
  *    once (round to nearest even).  Routing compares the raw fp32 logits and
