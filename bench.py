@@ -11,8 +11,19 @@ reported beside it.
 
 Prints one JSON line.  --config picks another workload (toy_decode,
 dense_gemv_e2m3, wide_decode, batched_decode, prefill).
+
+HBM traffic.  `roofline.traffic` comes from two rocprofv3 counter runs of
+`bench.py --profile-steps N` (FETCH_SIZE, then WRITE_SIZE).  Each such run
+ends with an elementwise copy of COPY_BYTES, whose counters calibrate the
+per-dispatch figures.  `bench.py --traffic-summary FETCH.csv WRITE.csv` turns
+the two counter files into a text summary under profiles/, stamped with a hash
+of the kernel sources; the JSON line carries the traffic only while that hash
+matches the sources it was built from, and null otherwise.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +37,16 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "wide_decode"
+COPY_BYTES = 512 << 20           # calibration copy: reads and writes this many bytes
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_of(workload, batch=1):
+    """The dominant kernel of a workload (the one the roofline is quoted for)."""
+    if workload == "dense_gemv_e2m3":
+        return "gemv_reg_kernel" if batch == 1 else "gemv_ring_kernel"
+    return {"wide_decode": "decode1_kernel", "toy_decode": "decode1_kernel",
+            "batched_decode": "decode_kernel", "prefill": "pf_gemm_kernel"}.get(workload, "kernel")
 
 
 def parse():
@@ -40,8 +61,106 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     p.add_argument("--profile-steps", type=int, default=0,
-                   help="only run this many eager steps after warmup (for rocprofv3 counter runs)")
+                   help="only run this many eager steps after warmup, then the calibration copy "
+                        "(for rocprofv3 counter runs)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the HBM traffic summary of two counter runs to profiles/ and exit")
+    p.add_argument("--command", default="", help="command line recorded in the traffic summary")
     return p.parse_args()
+
+
+def sources_hash():
+    """Hash of the HIP sources: a traffic summary is valid only for the kernels it measured."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_scaled_bit_moe_amd", "csrc", "*"))):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload, batch):
+    tag = workload if workload != "dense_gemv_e2m3" else "%s_b%d" % (workload, batch)
+    return os.path.join(PROFILES, "traffic_%s_%s.txt" % (kernel_of(workload, batch), tag))
+
+
+def copy_calibration(torch):
+    """An elementwise copy of known size (reads COPY_BYTES, writes COPY_BYTES)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def read_counters(path, counter):
+    """{kernel name: [per-dispatch values of `counter`]} from a rocprofv3 counter CSV."""
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic_summary(a):
+    cfg_name, batch = a.config, a.batch
+    want = kernel_of(cfg_name, batch)
+    fetch = read_counters(a.traffic_summary[0], "FETCH_SIZE")
+    write = read_counters(a.traffic_summary[1], "WRITE_SIZE")
+
+    def pick(d, key):
+        names = [n for n in d if key in n]
+        if not names:
+            raise SystemExit("no kernel matching %r in the counter file" % key)
+        vals = [v for n in names for v in d[n]]
+        return names, vals
+    kn, kf = pick(fetch, want)
+    _, kw = pick(write, want)
+    ckey = "neg_kernel" if any("neg_kernel" in n for n in fetch) else "elementwise_kernel"
+    _, cf = pick(fetch, ckey)
+    _, cw = pick(write, ckey)
+    copy_kib = COPY_BYTES / 1024.0
+    ff = copy_kib / cf[-1]
+    wf = copy_kib / cw[-1]
+    mf, mw = sum(kf) / len(kf), sum(kw) / len(kw)
+    traffic = (mf * ff + mw * wf) * 1024.0
+    os.makedirs(PROFILES, exist_ok=True)
+    path = traffic_file(cfg_name, batch)
+    with open(path, "w") as f:
+        f.write("# HBM traffic per dispatch of %s on %s (rocprofv3 --pmc, one counter per run)\n" % (want, cfg_name))
+        f.write("# command: %s\n" % a.command)
+        f.write("kernel: %s\n" % kn[0])
+        f.write("dispatches: %d\n" % len(kf))
+        f.write("fetch_kib_per_dispatch: %.1f\n" % mf)
+        f.write("write_kib_per_dispatch: %.1f\n" % mw)
+        f.write("copy_bytes: %d\n" % COPY_BYTES)
+        f.write("copy_fetch_kib: %.1f\n" % cf[-1])
+        f.write("copy_write_kib: %.1f\n" % cw[-1])
+        f.write("fetch_factor: %.4f\n" % ff)
+        f.write("write_factor: %.4f\n" % wf)
+        f.write("traffic_bytes_per_dispatch: %.0f\n" % traffic)
+        f.write("sources_sha256_16: %s\n" % sources_hash())
+    print(open(path).read())
+
+
+def measured_traffic(workload, batch):
+    """Calibrated HBM bytes per dispatch from the committed summary, or None when
+    there is none or the kernels changed since it was taken."""
+    path = traffic_file(workload, batch)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256_16") != sources_hash():
+        return None
+    return float(kv["traffic_bytes_per_dispatch"])
 
 
 def bytes_per_expert(cfg, inter):
@@ -109,8 +228,8 @@ def cpu_baseline_moe(cfg, seconds, logits_list, x):
     cache = {}
     sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
     spent, done = 0.0, 0
-    while done < len(logits_list) and spent < seconds:
-        l = logits_list[done]
+    while spent < seconds:
+        l = logits_list[done % len(logits_list)]
         idx, _ = oracle.route(l, cfg.top_k)
         ex = {}
         for e in np.unique(idx):
@@ -128,6 +247,9 @@ def cpu_baseline_moe(cfg, seconds, logits_list, x):
 
 def main():
     a = parse()
+    if a.traffic_summary:
+        traffic_summary(a)
+        return
     if a.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(expert sharding over RCCL is a design note, not code)", file=sys.stderr)
@@ -164,6 +286,7 @@ def main():
             for i in range(a.warmup + a.profile_steps):
                 calls[i % len(calls)]()
             torch.cuda.synchronize()
+            copy_calibration(torch)
             return
         secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
         per = secs / a.steps
@@ -172,7 +295,7 @@ def main():
         metric_value = tokens_per_s
         workload = {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols, "batch": B, "fmt": "e2m3+ue8m0/128",
                     "replicas": R}
-        kernel = "gemv_kernel"
+        kernel = kernel_of(cfg.name, B)
         cpu = None
         if not a.no_cpu_baseline:
             import oracle
@@ -222,6 +345,7 @@ def main():
                 calls[i % len(calls)]()
             torch.cuda.synchronize()
             moeq.moe_workspace_status(ws)
+            copy_calibration(torch)
             return
         secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
         moeq.moe_workspace_status(ws)
@@ -238,7 +362,7 @@ def main():
                     "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
                     "fmt": "e2m1+e4m3/16", "replicas": R, "logit_sets": NL,
                     "experts_read_per_call": float(np.mean(used))}
-        kernel = "decode_kernel"
+        kernel = kernel_of(cfg.name)
         cpu = None
         if not a.no_cpu_baseline:
             done, el = cpu_baseline_moe(cfg, a.cpu_seconds, logits_host, xh)
@@ -246,6 +370,7 @@ def main():
                    "sample": "%d call(s) of the same workload (%d token(s) each, fresh logits); %.1f s of "
                              "oracle time" % (done, T, el)}
 
+    traffic = measured_traffic(cfg.name, a.batch)
     line = {
         "metric": "MoE decode layer tokens/s and effective weight GB/s (% of 8 TB/s HBM)",
         "value": metric_value,
@@ -262,7 +387,7 @@ def main():
         "config": dict(workload, launch=mode),
         "effective_weight_GBps": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

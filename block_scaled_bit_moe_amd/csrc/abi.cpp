@@ -61,7 +61,9 @@ int moeq::decoder_choice() {
     static int choice = -1;
     if (choice < 0) {
         const char *v = getenv("MOEQ_DECODER");
-        choice = (v && !strcmp(v, "hw")) ? DEC_HW : DEC_LUT;
+        // The hardware conversions are the default: they decode a unit in fewer
+        // instructions and leave LDS free; the table decoder stays selectable.
+        choice = (v && !strcmp(v, "lut")) ? DEC_LUT : DEC_HW;
     }
     return choice;
 }

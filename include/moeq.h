@@ -99,7 +99,8 @@ enum {
     MOE_DECODER_LUT = 1 << 28,  /* decode codes through byte-indexed tables in LDS */
     MOE_DECODER_HW = 1 << 29,   /* decode codes with gfx950's fp4/fp6 -> bf16 conversions
                                    (both decoders are exact and give identical results; with
-                                   neither flag the library default is used) */
+                                   neither flag the library default is used: the hardware
+                                   decoder, unless the environment sets MOEQ_DECODER=lut) */
     MOE_DEBUG_SPIN_LIMIT = 1 << 30  /* test hook: inter-workgroup waits give up almost at once,
                                        so the MOE_EKERNEL path can be exercised; output invalid */
 };
