@@ -120,9 +120,7 @@ static LayerArgs layer_args(const moe_layer *L) {
 }
 
 static int decode_supported(const moe_layer *L, int T) {
-    if (T > DEC_MAX_T)
-        return fail(MOE_EUNSUPPORTED, "T=%d: more than %d tokens needs the prefill path, not in this build", T,
-                    DEC_MAX_T);
+    if (T > DEC_MAX_T) return MOE_OK;   // many-token path: no further limits
     if (L->hidden > DEC_MAX_DIM || L->inter > DEC_MAX_DIM || L->shared_inter > DEC_MAX_DIM)
         return fail(MOE_EUNSUPPORTED, "hidden/inter/shared_inter above %d are not supported by the decode kernels",
                     DEC_MAX_DIM);
@@ -130,7 +128,14 @@ static int decode_supported(const moe_layer *L, int T) {
 }
 
 static size_t ws_need(const moe_layer *L, int T) {
+    if (T > DEC_MAX_T)
+        return prefill_workspace_bytes(T, L->hidden, L->inter, L->shared_inter, L->top_k, L->n_experts);
     return decode_workspace_bytes(T, L->hidden, L->inter, L->shared_inter, L->top_k);
+}
+
+static hipError_t launch_layer(const DecodeArgs &a, int dec, hipStream_t s) {
+    if (a.T > DEC_MAX_T) return launch_prefill(a, s);   // always the hardware decoder (same values)
+    return launch_decode(a, dec, s);
 }
 
 extern "C" {
@@ -191,7 +196,7 @@ int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void 
     a.fixed_e = expert;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
-    hipError_t e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
+    hipError_t e = launch_layer(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_expert_ffn_q launch", e);
     return ok();
 }
@@ -221,7 +226,7 @@ int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int
     a.fixed_e = 0;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
-    hipError_t e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
+    hipError_t e = launch_layer(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_layer_decode launch", e);
     return ok();
 }

@@ -52,6 +52,11 @@ constexpr int DEC_S2 = 64;         // output rows per down item
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k);
 
+// Many-token path (T > DEC_MAX_T): tokens are processed in chunks of PF_CHUNK.
+constexpr int PF_CHUNK = 2048;
+size_t prefill_workspace_bytes(int T, int H, int I, int Ish, int k, int E);
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s);
+
 // Lanes per row of the down projection: one mapping for every expert of the
 // layer (set by the smaller intermediate size), so a token's arithmetic does
 // not depend on which kernel or which other tokens share the call.

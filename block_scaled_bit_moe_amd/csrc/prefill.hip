@@ -1,0 +1,103 @@
+// prefill.hip -- host side of the many-token MoE layer: workspace layout,
+// chunking of the tokens and the five launches per chunk.
+#include "prefill.h"
+
+namespace moeq {
+
+// Workspace of one chunk of Tc tokens, after the shared header.
+struct PfLayout {
+    size_t idx, w, rank, cnt, off, nblk, blk, tok, h_hi, h_lo, y, total;
+    int Tc, NS, pairs, nblk_max;
+};
+
+static size_t align256(size_t v) { return (v + 255u) & ~(size_t)255u; }
+
+static PfLayout pf_layout(int T, int H, int I, int Ish, int k, int E) {
+    PfLayout l;
+    l.Tc = T < PF_CHUNK ? T : PF_CHUNK;
+    l.NS = E + (Ish > 0 ? 1 : 0);
+    l.pairs = l.Tc * (k + 1);
+    l.nblk_max = ((l.pairs + (PF_MB - 1) * l.NS) / PF_MB + 8) & ~7;
+    const size_t Imax = (size_t)(I > Ish ? I : Ish);
+    // after everything the decode kernels use, so one workspace serves both
+    // paths and nothing written here can pass for a tagged word of the
+    // single-token kernel
+    size_t o = align256(decode_workspace_bytes(DEC_MAX_T, H, I, Ish, k));
+    auto take = [&](size_t bytes) {
+        const size_t r = o;
+        o = align256(o + bytes);
+        return r;
+    };
+    l.idx = take((size_t)l.Tc * k * 4);
+    l.w = take((size_t)l.Tc * k * 4);
+    l.rank = take((size_t)l.Tc * k * 4);
+    l.cnt = take((size_t)(l.NS + 1) * 4);
+    l.off = take((size_t)(l.NS + 1) * 4);
+    l.nblk = take(4);
+    l.blk = take((size_t)l.nblk_max * 4);
+    l.tok = take((size_t)l.NS * l.Tc * 4);
+    l.h_hi = take((size_t)l.pairs * Imax * 2);
+    l.h_lo = take((size_t)l.pairs * Imax * 2);
+    l.y = take((size_t)l.pairs * H * 4);
+    l.total = o;
+    return l;
+}
+
+size_t prefill_workspace_bytes(int T, int H, int I, int Ish, int k, int E) {
+    return pf_layout(T, H, I, Ish, k, E).total;
+}
+
+template <int FMT>
+static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
+    const int Imax = p.L.I > p.L.Ish ? p.L.I : p.L.Ish;
+    const int nt_gu = (Imax + 64 * PF_RG_GU - 1) / (64 * PF_RG_GU);
+    const int nt_dn = (p.L.H + 64 * PF_RG_DN - 1) / (64 * PF_RG_DN);
+    hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(PF_THREADS), 0, s, p, nt_gu);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(PF_THREADS), 0, s, p, nt_dn);
+    hipLaunchKernelGGL(pf_combine_kernel, dim3(p.T), dim3(PF_THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
+    const LayerArgs &L = a.L;
+    const PfLayout l = pf_layout(a.T, L.H, L.I, L.Ish, L.k, L.E);
+    uint8_t *ws = a.ws;
+    const size_t out_elt = a.out_f32 ? 4 : 2;
+    for (int c0 = 0; c0 < a.T; c0 += l.Tc) {
+        const int Tc = (a.T - c0) < l.Tc ? (a.T - c0) : l.Tc;
+        PfArgs p;
+        p.L = L;
+        p.x = a.x + (size_t)c0 * L.H;
+        p.T = Tc;
+        p.NS = l.NS;
+        p.mode = a.mode;
+        p.fixed_e = a.fixed_e;
+        int32_t *idx = a.idx_out ? a.idx_out + (size_t)c0 * L.k : (int32_t *)(ws + l.idx);
+        float *w = a.w_out ? a.w_out + (size_t)c0 * L.k : (float *)(ws + l.w);
+        p.idx = idx;
+        p.w = w;
+        p.rank = (int32_t *)(ws + l.rank);
+        p.cnt = (int32_t *)(ws + l.cnt);
+        p.off = (int32_t *)(ws + l.off);
+        p.nblk = (int32_t *)(ws + l.nblk);
+        p.blk = (int32_t *)(ws + l.blk);
+        p.tok = (int32_t *)(ws + l.tok);
+        p.h_hi = (uint16_t *)(ws + l.h_hi);
+        p.h_lo = (uint16_t *)(ws + l.h_lo);
+        p.y = (float *)(ws + l.y);
+        p.out = (uint8_t *)a.out + (size_t)c0 * L.H * out_elt;
+        p.out_f32 = a.out_f32;
+        p.hdr = (uint32_t *)ws;
+        p.Imax = L.I > L.Ish ? L.I : L.Ish;
+        if (a.mode == MODE_ROUTE) {
+            hipError_t e = launch_route(a.logits + (size_t)c0 * L.E, Tc, L.E, L.k, idx, w, s);
+            if (e != hipSuccess) return e;
+        }
+        hipError_t e = L.fmt == 1 ? pf_chunk<FMT_E2M1>(p, l, s) : pf_chunk<FMT_E2M3>(p, l, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace moeq

@@ -109,6 +109,23 @@ def test_workspace_bytes_and_checks(lib):
                                 None) == moeq.MOE_EINVAL
 
 
+def test_many_token_workspace(lib):
+    """T > 16 takes the many-token path: its workspace grows with the chunk
+    (at most 2,048 tokens) and a smaller workspace is refused."""
+    L = _layer()
+    n = ctypes.c_size_t(0)
+    sizes = {}
+    for T in (16, 17, 2048, 2049, 65536):
+        assert lib.moe_layer_workspace_bytes(ctypes.byref(L), T, ctypes.byref(n)) == moeq.MOE_OK
+        sizes[T] = n.value
+    assert sizes[17] < sizes[2048] == sizes[2049] == sizes[65536]
+    H, I, k = L.hidden, max(L.inter, L.shared_inter), L.top_k
+    assert sizes[2048] >= 2048 * (k + 1) * (H * 4 + I * 4)      # fp32 partials + h pair per (token, expert)
+    assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 17, FAKE, None, None, 0, FAKE2, sizes[17] - 1,
+                                None) == moeq.MOE_EWORKSPACE
+    assert "needs" in _err(lib)
+
+
 def test_expert_ffn_validation(lib):
     L = _layer()
     n = ctypes.c_size_t(0)
