@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 DEFAULT_CONFIG = "wide_decode"
 COPY_BYTES = 512 << 20           # calibration copy: reads and writes this many bytes
 PROFILES = os.path.join(ROOT, "profiles")
@@ -46,7 +47,7 @@ def kernel_of(workload, batch=1):
     if workload == "dense_gemv_e2m3":
         return "gemv_reg_kernel" if batch == 1 else "gemv_ring_kernel"
     return {"wide_decode": "decode1_kernel", "toy_decode": "decode1_kernel",
-            "batched_decode": "decode_kernel", "prefill": "pf_gemm_kernel"}.get(workload, "kernel")
+            "batched_decode": "decode_kernel", "prefill": "layer_step"}.get(workload, "kernel")
 
 
 def parse():
@@ -117,8 +118,19 @@ def traffic_summary(a):
             raise SystemExit("no kernel matching %r in the counter file" % key)
         vals = [v for n in names for v in d[n]]
         return names, vals
-    kn, kf = pick(fetch, want)
-    _, kw = pick(write, want)
+    if want == "layer_step":
+        # the many-token step is five launches: sum them, per step
+        def step(d):
+            names = [n for n in d if "pf_" in n or "route_kernel" in n]
+            steps = sum(len(d[n]) for n in names if "pf_group" in n)
+            if not steps:
+                raise SystemExit("no many-token step in the counter file")
+            return names, [sum(v for n in names for v in d[n]) / steps] * steps
+        kn, kf = step(fetch)
+        _, kw = step(write)
+    else:
+        kn, kf = pick(fetch, want)
+        _, kw = pick(write, want)
     ckey = "neg_kernel" if any("neg_kernel" in n for n in fetch) else "elementwise_kernel"
     _, cf = pick(fetch, ckey)
     _, cw = pick(write, ckey)
@@ -132,7 +144,7 @@ def traffic_summary(a):
     with open(path, "w") as f:
         f.write("# HBM traffic per dispatch of %s on %s (rocprofv3 --pmc, one counter per run)\n" % (want, cfg_name))
         f.write("# command: %s\n" % a.command)
-        f.write("kernel: %s\n" % kn[0])
+        f.write("kernel: %s\n" % (" + ".join(sorted(kn)) if want == "layer_step" else kn[0]))
         f.write("dispatches: %d\n" % len(kf))
         f.write("fetch_kib_per_dispatch: %.1f\n" % mf)
         f.write("write_kib_per_dispatch: %.1f\n" % mw)
@@ -219,17 +231,24 @@ def run_steps(torch, calls, steps, warmup, eager):
     return t.stop(), "hipgraph"
 
 
-def cpu_baseline_moe(cfg, seconds, logits_list, x):
+def cpu_baseline_moe(cfg, seconds, logits_list, x, slice_tokens=None):
     """The oracle on the host cores, call after call of the same workload, until
-    ~`seconds` of oracle time.  Generating the selected experts' bytes on the
-    host is not timed.  Returns (calls, oracle seconds)."""
+    ~`seconds` of oracle time.  With slice_tokens, each call takes the next
+    slice of that many tokens of the workload (for workloads whose full call
+    would take the oracle minutes).  Generating the selected experts' bytes on
+    the host is not timed.  Returns (tokens done, oracle seconds)."""
     import oracle
     import synth
     cache = {}
     sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
-    spent, done = 0.0, 0
+    spent, done, tokens = 0.0, 0, 0
+    T = x.shape[0]
     while spent < seconds:
         l = logits_list[done % len(logits_list)]
+        xs = x
+        if slice_tokens:
+            t0 = (done * slice_tokens) % T
+            l, xs = l[t0:t0 + slice_tokens], x[t0:t0 + slice_tokens]
         idx, _ = oracle.route(l, cfg.top_k)
         ex = {}
         for e in np.unique(idx):
@@ -238,11 +257,12 @@ def cpu_baseline_moe(cfg, seconds, logits_list, x):
                 cache[e] = synth.expert_weights(cfg, e)
             ex[e] = cache[e]
         t1 = time.perf_counter()
-        oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, x, l, shared=sh,
+        oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xs, l, shared=sh,
                      shared_inter=cfg.shared_inter)
         spent += time.perf_counter() - t1
         done += 1
-    return done, spent
+        tokens += xs.shape[0]
+    return tokens, spent
 
 
 def main():
@@ -313,8 +333,7 @@ def main():
                    "weight_GBps": frac * wbytes / el / 1e9}
     else:
         T = cfg.tokens
-        if T > moeq.MAX_DECODE_TOKENS:
-            print("config %s needs the prefill path" % cfg.name, file=sys.stderr)
+        many = T > moeq.MAX_DECODE_TOKENS
         per_expert = bytes_per_expert(cfg, cfg.inter)
         layer_bytes = cfg.experts * per_expert
         R = a.replicas or max(1, min(32, -(-(4 << 30) // layer_bytes)))
@@ -330,7 +349,7 @@ def main():
                 sh = dict(zip(("w13_codes", "w13_scales", "w2_codes", "w2_scales"), [tt.clone() for tt in L0.tensors[4:]]))
             layers.append(moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, *t,
                                      shared_inter=cfg.shared_inter, shared=sh))
-        NL = 64
+        NL = 64 if not many else 4
         logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
         logits = [torch.from_numpy(l).cuda() for l in logits_host]
         xh = synth.hidden_states(cfg)
@@ -364,11 +383,20 @@ def main():
                     "experts_read_per_call": float(np.mean(used))}
         kernel = kernel_of(cfg.name)
         cpu = None
+        if many:
+            # the matrix-core work of the step: 2 flops per multiply-add of gate, up and down
+            pairs = T * (cfg.top_k + (1 if cfg.shared_inter else 0))
+            flops = 2.0 * T * cfg.top_k * 3 * cfg.hidden * cfg.inter
+            if cfg.shared_inter:
+                flops += 2.0 * T * 3 * cfg.hidden * cfg.shared_inter
+            workload["pairs"] = pairs
+            workload["mfma_tflops_algorithmic"] = flops / per / 1e12
+            workload["mfma_frac_of_bf16_dense_peak"] = flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS
         if not a.no_cpu_baseline:
-            done, el = cpu_baseline_moe(cfg, a.cpu_seconds, logits_host, xh)
-            cpu = {"value": done * T / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
-                   "sample": "%d call(s) of the same workload (%d token(s) each, fresh logits); %.1f s of "
-                             "oracle time" % (done, T, el)}
+            tok, el = cpu_baseline_moe(cfg, a.cpu_seconds, logits_host, xh, slice_tokens=16 if many else None)
+            cpu = {"value": tok / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
+                   "sample": "%d token(s) of the workload (%s, fresh logits); %.1f s of oracle time" %
+                             (tok, "slices of 16 tokens of the chunk" if many else "whole calls", el)}
 
     traffic = measured_traffic(cfg.name, a.batch)
     line = {

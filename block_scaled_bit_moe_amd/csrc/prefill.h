@@ -34,13 +34,17 @@
 // distinct banks), double-buffered, and read by all four waves.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
+#include "stream.h"
 
 namespace moeq {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f2_t;
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_MB = 64;                   // tokens per block (four 16-row sub-tiles)
@@ -175,42 +179,289 @@ __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
     }
 }
 
-// bf16 pair times a block scale; exact because the products fit in bf16.
-__device__ inline u32 pf_scale_pair(u32 p, float s) {
-    const float lo = __builtin_bit_cast(float, p << 16) * s;
-    const float hi = __builtin_bit_cast(float, p & 0xFFFF0000u) * s;
-    return (__builtin_bit_cast(u32, hi) & 0xFFFF0000u) | (__builtin_bit_cast(u32, lo) >> 16);
+// Weight units of one K step for the NB row groups of a lane.  Addresses are
+// clamped into the row so the loads need no branch (the compiler can then
+// count outstanding loads exactly); units past the row's end are zeroed at
+// conversion.
+template <int FMT>
+__device__ inline Unit<FMT> pf_load_unit(const uint8_t *rc, const uint8_t *rs, int u) {
+    Unit<FMT> U;
+    load_unit<FMT>(U, rc, rs, u);
+    return U;
 }
 
-// Decode one unit into the B operands of the four MFMA steps of a K step.
+// Decode one unit, block scale included, into the B operands of the four MFMA
+// steps of a K step (step s takes weights 8s .. 8s+7 of the unit).
+//  e2m1 + e4m3: each byte -> two fp32 values, times the scale (exact: a code
+//    value times an e4m3 scale has at most 5 significant bits), packed to bf16;
+//  e2m3 + UE8M0: the 32-value conversion applies the power-of-two scale
+//    itself (the conversion takes the scale's exponent field, which is all a
+//    UE8M0 scale has).
 template <int FMT>
-__device__ inline void pf_unit_to_b(const Unit<FMT> &U, const Luts &Lt, bool valid, bf16x8_t (&b)[4]) {
-    u32 w[16];
-    decode_unit<FMT, DEC_HW>(U, Lt, w);
-    float s0, s1;
-    unit_scales<FMT>(U, Lt, s0, s1);
-    if constexpr (FMT == FMT_E2M3) s1 = s0;
+__device__ inline void pf_unit_to_b(const Unit<FMT> &U, const float *s_scale, bf16x8_t (&b)[4]) {
+    if constexpr (FMT == FMT_E2M1) {
+        const float s0 = s_scale[U.s & 0xFF], s1 = s_scale[(U.s >> 8) & 0xFF];
+        const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const float sc = s < 2 ? s0 : s1;
-        u32x4_t v;
-        v[0] = valid ? pf_scale_pair(w[4 * s + 0], sc) : 0u;
-        v[1] = valid ? pf_scale_pair(w[4 * s + 1], sc) : 0u;
-        v[2] = valid ? pf_scale_pair(w[4 * s + 2], sc) : 0u;
-        v[3] = valid ? pf_scale_pair(w[4 * s + 3], sc) : 0u;
-        b[s] = __builtin_bit_cast(bf16x8_t, v);
+        for (int s = 0; s < 4; ++s) {
+            const float sc = s < 2 ? s0 : s1;
+            const f2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 0);
+            const f2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 1);
+            const f2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 2);
+            const f2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 3);
+            const bf16x2_t p[4] = {bf16x2_t{(__bf16)(f0.x * sc), (__bf16)(f0.y * sc)},
+                                   bf16x2_t{(__bf16)(f1.x * sc), (__bf16)(f1.y * sc)},
+                                   bf16x2_t{(__bf16)(f2.x * sc), (__bf16)(f2.y * sc)},
+                                   bf16x2_t{(__bf16)(f3.x * sc), (__bf16)(f3.y * sc)}};
+            u32x4_t v;
+            v[0] = __builtin_bit_cast(u32, p[0]);
+            v[1] = __builtin_bit_cast(u32, p[1]);
+            v[2] = __builtin_bit_cast(u32, p[2]);
+            v[3] = __builtin_bit_cast(u32, p[3]);
+            b[s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    } else {
+        u32x6_t v;
+        v[0] = U.c0.x; v[1] = U.c0.y; v[2] = U.c1.x; v[3] = U.c1.y; v[4] = U.c2.x; v[5] = U.c2.y;
+        const float sc = __builtin_bit_cast(float, (U.s & 0xFFu) << 23);
+        const bf16x32_t r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(v, sc);
+        typedef __attribute__((ext_vector_type(16))) u32 u32x16_t;
+        const u32x16_t rr = __builtin_bit_cast(u32x16_t, r);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4_t q;
+            q[0] = rr[4 * s]; q[1] = rr[4 * s + 1]; q[2] = rr[4 * s + 2]; q[3] = rr[4 * s + 3];
+            b[s] = __builtin_bit_cast(bf16x8_t, q);
+        }
     }
 }
 
-// Grouped GEMM over the block list.  DOWN = false: gate/up with the SiLU
-// epilogue (NB = 2 * RG weight row groups per wave: RG of gate, RG of up);
-// DOWN = true: down projection from the h pair (NB = RG).
+template <int FMT>
+__device__ inline void pf_zero_unit(Unit<FMT> &U) {
+    if constexpr (FMT == FMT_E2M1) {
+        U.c = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        U.c0 = make_uint2(0u, 0u);
+        U.c1 = U.c0;
+        U.c2 = U.c0;
+    }
+    U.s = 0u;
+}
+
+// Barrier without the release/acquire fences of __syncthreads(): those make
+// the compiler drain every outstanding vector load (vmcnt(0)), which would
+// empty the prefetch pipeline at each step.  Callers wait for exactly the
+// loads they need first; the memory clobbers keep the compiler from moving
+// LDS accesses across the barrier.
+__device__ inline void pf_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ inline void pf_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Vector-memory loads of one weight unit.
+template <int FMT> struct PfUnitLoads { static constexpr int n = FMT == FMT_E2M1 ? 2 : 4; };
+
+// Grouped GEMM main loop for a block of NSUB 16-token sub-tiles.
+//
+// Pipeline.  K step j needs (i) the activation tile of step j, copied from
+// HBM/L2 straight into an LDS stage by buffer-load-to-LDS, and (ii) each
+// lane's weight units of step j, in registers.  Both are issued together, PD
+// steps ahead, into a ring of PD + 1 LDS stages and PD register slots.
+// Vector-memory loads of a wave complete in issue order, so "step j landed"
+// is one s_waitcnt vmcnt(loads issued after step j's group); the barrier
+// that follows makes every wave's copy of stage j visible, and since the
+// next copy is issued after that barrier it only overwrites the stage all
+// waves finished reading one step earlier.
+//
+// Activation stage layout: plane pl (x, or h_hi / h_lo), rows 16 * NSUB of
+// 256 bytes (128 bf16); the 16-byte piece c of row r sits at c ^ (r & 15), so
+// the 16 rows a quarter-wave reads for one MFMA hit 16 different bank groups.
+template <int FMT, bool DOWN, int NSUB, int NWAVES, int RG>
+__device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2, uint8_t *st3,
+                                    const float *s_scale, const int *s_tok, int M,
+                                    int p0, int K, int N, int n0, const uint8_t *const (&rc)[DOWN ? RG : 2 * RG],
+                                    const uint8_t *const (&rs)[DOWN ? RG : 2 * RG]) {
+    constexpr int NB = DOWN ? RG : 2 * RG;
+    constexpr int NPL = DOWN ? 2 : 1;
+    constexpr int PLANE = NSUB * 16 * 256;                  // bytes per plane of a stage
+    constexpr int R = PF_PD + 1;                            // stages in the ring (separate LDS objects)
+    static_assert(R == 4, "four stage objects");
+    constexpr int NDMA = NSUB * 4 * NPL;                    // 1 KiB copies per stage
+    static_assert(NDMA % NWAVES == 0, "copies per wave");
+    constexpr int DPW = NDMA / NWAVES;                      // per wave
+    constexpr int PER_GROUP = DPW + NB * PfUnitLoads<FMT>::n;   // loads a wave issues per step
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int H = a.L.H;
+    const int nK = (K + PF_KS - 1) / PF_KS;
+    const int UK = K / 32;
+
+    // the activation copies of this lane: byte offset of its row's first
+    // element (plus its piece's column) in the source buffer
+    __amdgpu_buffer_rsrc_t src[NPL];
+    if (DOWN) {
+        const uint64_t bytes = (uint64_t)a.off[a.NS] * a.Imax * 2;
+        src[0] = rsrc_of(a.h_hi, bytes);
+        src[NPL - 1] = rsrc_of(a.h_lo, bytes);
+    } else {
+        src[0] = rsrc_of(a.x, (uint64_t)a.T * H * 2);
+    }
+    u32 row_off[DPW], col_k[DPW];
+    int dst_off[DPW], dpl[DPW];
+#pragma unroll
+    for (int q = 0; q < DPW; ++q) {
+        const int g = q * NWAVES + wv;                      // copy index in the stage
+        const int pl = g / (NSUB * 4);
+        const int P = (g % (NSUB * 4)) * 64 + lane;         // 16-byte piece of the plane
+        const int row = P >> 4;
+        const int logical = (P & 15) ^ (row & 15);
+        const int rr = min(row, M - 1);
+        row_off[q] = DOWN ? (u32)(p0 + rr) * (u32)a.Imax * 2u : (u32)s_tok[rr] * (u32)H * 2u;
+        col_k[q] = (u32)logical * 8u;
+        dst_off[q] = pl * PLANE + (g % (NSUB * 4)) * 1024;
+        dpl[q] = pl;
+    }
+    // stage S of the ring; distinct objects, so the compiler can tell a copy
+    // into one stage from reads of another and need not wait between them
+    auto stage = [&](auto sc) -> uint8_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0) return st0;
+        else if constexpr (S == 1) return st1;
+        else if constexpr (S == 2) return st2;
+        else return st3;
+    };
+    auto issue_stage = [&](auto sc, int j) {
+        uint8_t *st = stage(sc);
+        const u32 kb = (u32)j * PF_KS;
+#pragma unroll
+        for (int q = 0; q < DPW; ++q) {
+            const u32 k = kb + col_k[q];
+            const u32 voff = k < (u32)K ? row_off[q] + k * 2u : 0x7FFFFFF0u;   // past K: reads as zeros
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src[dpl[q]], (lds_void_t *)(st + dst_off[q]), 16, voff, 0, 0, 0);
+        }
+    };
+
+    Unit<FMT> wq[R][NB];
+    auto load_w = [&](Unit<FMT> (&U)[NB], int j) {
+        const int u = min(j * 4 + lg, UK - 1);              // clamped: no branch, result unused past the end
+#pragma unroll
+        for (int b = 0; b < NB; ++b) load_unit<FMT>(U[b], rc[b], rs[b], u);
+    };
+
+    f32x4_t acc[NB][NSUB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // prologue: steps 0 .. PD-1 in flight
+    issue_stage(I0{}, 0);
+    load_w(wq[0], 0);
+    issue_stage(I1{}, 1);
+    load_w(wq[1], 1);
+    issue_stage(I2{}, 2);
+    load_w(wq[2], 2);
+
+    // step it uses stage and weight slot it % 4 and refills slot (it + 3) % 4
+    auto step = [&](auto dc, int it) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + PF_PD) % R;
+        pf_wait_vm<(PF_PD - 1) * PER_GROUP>();              // this wave's step-it loads have landed
+        pf_barrier();                                       // ... and every wave's; stage (it-1) % R is free
+        if (it * 4 + lg >= UK) {                            // units past the row's end: zero weights
+#pragma unroll
+            for (int j = 0; j < NB; ++j) pf_zero_unit<FMT>(wq[d][j]);
+        }
+        bf16x8_t bw[NB][4];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) pf_unit_to_b<FMT>(wq[d][j], s_scale, bw[j]);
+        issue_stage(std::integral_constant<int, dn>{}, it + PF_PD);
+        load_w(wq[dn], it + PF_PD);
+        const uint8_t *st = stage(dc);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int piece = ((lg * 4 + s) ^ lr) * 16;
+            bf16x8_t ah[NSUB], al[NSUB];
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+                const uint8_t *ap = st + (16 * m + lr) * 256 + piece;
+                ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
+                if (DOWN) al[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PLANE));
+            }
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bw[j][s], acc[j][m], 0, 0, 0);
+                    if (DOWN)
+                        acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bw[j][s], acc[j][m], 0, 0, 0);
+                }
+        }
+    };
+    int it = 0;
+    for (; it + R <= nK; it += R) {
+        step(I0{}, it);
+        step(I1{}, it + 1);
+        step(I2{}, it + 2);
+        step(I3{}, it + 3);
+    }
+    if (it < nK) step(I0{}, it);
+    if (it + 1 < nK) step(I1{}, it + 1);
+    if (it + 2 < nK) step(I2{}, it + 2);
+    // drain the copies issued past the end before the workgroup's LDS is reused
+    pf_wait_vm<0>();
+
+    // epilogue: lane holds rows (tokens) 16m + 4 lg + i, column (weight row) lr
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int n = n0 + wv * 16 * RG + g * 16 + lr;
+        if (n >= N) continue;
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * m + 4 * lg + i;
+                if (t >= M) continue;
+                const size_t p = (size_t)(p0 + t);
+                if (DOWN) {
+                    a.y[p * H + n] = acc[g][m][i];
+                } else {
+                    const float h = silu_f32(acc[g][m][i]) * acc[RG + g][m][i];
+                    const uint16_t hi = f32_to_bf16_rne(h);
+                    const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
+                    a.h_hi[p * a.Imax + n] = hi;
+                    a.h_lo[p * a.Imax + n] = lo;
+                }
+            }
+        }
+    }
+}
+
+// Grouped GEMM over the block list.  gate/up (DOWN = false): 4 waves, each
+// with 16 rows of gate and the same 16 rows of up; down: 8 waves of 32 rows.
 template <int FMT, bool DOWN>
-__global__ __launch_bounds__(PF_THREADS, 2) void pf_gemm_kernel(PfArgs a, int NT) {
+__global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel(PfArgs a, int NT) {
+    constexpr int NWAVES = DOWN ? 8 : 4;
     constexpr int RG = DOWN ? PF_RG_DN : PF_RG_GU;
     constexpr int NB = DOWN ? RG : 2 * RG;
-    constexpr int NPL = DOWN ? 2 : 1;        // staged activation planes (hi, lo)
-    __shared__ __attribute__((aligned(16))) uint8_t pf_smem[2 * NPL * PF_STAGE];
+    constexpr int NPL = DOWN ? 2 : 1;
+    constexpr int ROWS_WG = NWAVES * 16 * RG;
+    constexpr int STAGE_BYTES = NPL * 4 * 16 * 256;
+    __shared__ __attribute__((aligned(1024))) uint8_t pf_st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t pf_st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t pf_st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t pf_st3[STAGE_BYTES];
     __shared__ float s_scale[LUT_SCALE];
     __shared__ int s_tok[PF_MB];
 
@@ -226,19 +477,21 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gemm_kernel(PfArgs a, int NT
     const int Is = shared ? a.L.Ish : a.L.I;
     const int N = DOWN ? H : Is;
     const int K = DOWN ? Is : H;
-    const int n0 = nt * 64 * RG;
+    const int n0 = nt * ROWS_WG;
     if (n0 >= N) return;
     const int M = min(PF_MB, a.cnt[slot] - m0);
     const int nsub = (M + 15) >> 4;
     const int p0 = a.off[slot] + m0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int lg = lane >> 4, lr = lane & 15;
+    const int lr = lane & 15;
 
-    Luts Lt;
-    Lt.pair = nullptr;
-    Lt.scale = s_scale;
-    build_luts<FMT>(Lt, tid, PF_THREADS, false);
-    if (tid < PF_MB) s_tok[tid] = a.tok[(size_t)slot * a.T + m0 + min(tid, M - 1)];
+    if (FMT == FMT_E2M1) {
+        Luts Lt;
+        Lt.pair = nullptr;
+        Lt.scale = s_scale;
+        build_luts<FMT>(Lt, tid, NWAVES * 64, false);
+    }
+    if (!DOWN && tid < PF_MB) s_tok[tid] = a.tok[(size_t)slot * a.T + m0 + min(tid, M - 1)];
 
     // weight rows of this wave
     using F = Fmt<FMT>;
@@ -256,135 +509,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void pf_gemm_kernel(PfArgs a, int NT
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int g = DOWN ? j : (j % RG);
-        int n = n0 + wv * 16 * RG + g * 16 + lr;
-        n = min(n, N - 1);                      // rows past N: a valid row, result dropped
+        const int n = min(n0 + wv * 16 * RG + g * 16 + lr, N - 1);   // rows past N: a valid row, result dropped
         const int row = (!DOWN && j >= RG) ? Is + n : n;
         rc[j] = wc + (size_t)row * crb;
         rs[j] = ws + (size_t)row * srb;
     }
-    const int nK = (K + PF_KS - 1) / PF_KS;
-    const int UK = K / 32;                      // units per row
-
-    // activation staging: thread t moves 16-byte pieces c = t + 256 i of the tile
-    // (row c / 16, piece c % 16 = k offset 8 * (c % 16)); rows >= 16 * nsub are skipped
-    auto stage_src = [&](int c, int pl) -> const uint16_t * {
-        const int row = c >> 4;
-        if (DOWN) {
-            const int p = p0 + min(row, M - 1);
-            return (pl == 0 ? a.h_hi : a.h_lo) + (size_t)p * a.Imax;
-        }
-        return a.x + (size_t)s_tok[row] * H;
-    };
-    uint4 st[NPL][4];
-    auto stage_load = [&](int kb) {
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = tid + PF_THREADS * i;
-                const int row = c >> 4, kk = kb + (c & 15) * 8;
-                if (row < nsub * 16 && kk < K) st[pl][i] = *reinterpret_cast<const uint4 *>(stage_src(c, pl) + kk);
-                else st[pl][i] = make_uint4(0u, 0u, 0u, 0u);
-            }
-    };
-    auto stage_store = [&](int buf) {
-#pragma unroll
-        for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = tid + PF_THREADS * i;
-                uint8_t *d = pf_smem + (size_t)(buf * NPL + pl) * PF_STAGE + (c >> 4) * PF_ROW + (c & 15) * 16;
-                *reinterpret_cast<uint4 *>(d) = st[pl][i];
-            }
-    };
-
-    // weight units in flight: wq[d][j] holds K step (it + d) for row group j
-    Unit<FMT> wq[PF_PD][NB];
-    auto load_w = [&](Unit<FMT> (&U)[NB], int it) {
-        const int u = it * 4 + lg;
-        if (it < nK && u < UK) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j) load_unit<FMT>(U[j], rc[j], rs[j], u);
-        }
-    };
-
-    __syncthreads();   // s_tok, LUT
-#pragma unroll
-    for (int d = 0; d < PF_PD; ++d) load_w(wq[d], d);
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
-
-    f32x4_t acc[NB][4];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int it0 = 0; it0 < nK; it0 += PF_PD) {
-#pragma unroll
-        for (int d = 0; d < PF_PD; ++d) {
-            const int it = it0 + d;
-            if (it >= nK) break;
-            if (it + 1 < nK) stage_load((it + 1) * PF_KS);
-            const bool uvalid = it * 4 + lg < UK;
-            bf16x8_t bw[NB][4];
-#pragma unroll
-            for (int j = 0; j < NB; ++j) pf_unit_to_b<FMT>(wq[d][j], Lt, uvalid, bw[j]);
-            load_w(wq[d], it + PF_PD);
-            const uint8_t *abase = pf_smem + (size_t)((it & 1) * NPL) * PF_STAGE + lr * PF_ROW + lg * 64;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if (m < nsub) {
-                        const uint8_t *ap = abase + m * 16 * PF_ROW + s * 16;
-                        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
-                        if (DOWN) {
-                            const bf16x8_t a1 =
-                                __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PF_STAGE));
-#pragma unroll
-                            for (int j = 0; j < NB; ++j) {
-                                acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bw[j][s], acc[j][m], 0, 0, 0);
-                                acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bw[j][s], acc[j][m], 0, 0, 0);
-                            }
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < NB; ++j)
-                                acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bw[j][s], acc[j][m], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-            if (it + 1 < nK) stage_store((it + 1) & 1);
-            __syncthreads();
-        }
-    }
-
-    // epilogue: lane holds rows (tokens) 16m + 4 lg + i, column (weight row) lr
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        const int n = n0 + wv * 16 * RG + g * 16 + lr;
-        if (n >= N) continue;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m >= nsub) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * m + 4 * lg + i;
-                if (t >= M) continue;
-                const size_t p = (size_t)(p0 + t);
-                if (DOWN) {
-                    a.y[p * H + n] = acc[g][m][i];
-                } else {
-                    const float h = silu_f32(acc[g][m][i]) * acc[RG + g][m][i];
-                    const uint16_t hi = f32_to_bf16_rne(h);
-                    const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
-                    a.h_hi[p * a.Imax + n] = hi;
-                    a.h_lo[p * a.Imax + n] = lo;
-                }
-            }
-        }
+    __syncthreads();   // s_tok, scale table
+    switch (nsub) {
+        case 1: pf_gemm_main<FMT, DOWN, 1, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        case 2: pf_gemm_main<FMT, DOWN, 2, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        case 3: pf_gemm_main<FMT, DOWN, 3, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        default: pf_gemm_main<FMT, DOWN, 4, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
     }
 }
 

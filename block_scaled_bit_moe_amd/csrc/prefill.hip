@@ -14,11 +14,16 @@ static size_t align256(size_t v) { return (v + 255u) & ~(size_t)255u; }
 
 static PfLayout pf_layout(int T, int H, int I, int Ish, int k, int E) {
     PfLayout l;
-    l.Tc = T < PF_CHUNK ? T : PF_CHUNK;
+    const size_t Imax = (size_t)(I > Ish ? I : Ish);
+    // chunk: at most PF_CHUNK tokens, and small enough that the h pair of
+    // every (token, expert) pair stays below 2 GiB (32-bit buffer offsets)
+    size_t cap = ((size_t)1 << 31) / ((size_t)(k + 1) * Imax * 2);
+    cap = cap < 16 ? 16 : (cap & ~(size_t)15);
+    const int chunk = (int)(cap < (size_t)PF_CHUNK ? cap : (size_t)PF_CHUNK);
+    l.Tc = T < chunk ? T : chunk;
     l.NS = E + (Ish > 0 ? 1 : 0);
     l.pairs = l.Tc * (k + 1);
     l.nblk_max = ((l.pairs + (PF_MB - 1) * l.NS) / PF_MB + 8) & ~7;
-    const size_t Imax = (size_t)(I > Ish ? I : Ish);
     // after everything the decode kernels use, so one workspace serves both
     // paths and nothing written here can pass for a tagged word of the
     // single-token kernel
@@ -50,11 +55,12 @@ size_t prefill_workspace_bytes(int T, int H, int I, int Ish, int k, int E) {
 template <int FMT>
 static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     const int Imax = p.L.I > p.L.Ish ? p.L.I : p.L.Ish;
-    const int nt_gu = (Imax + 64 * PF_RG_GU - 1) / (64 * PF_RG_GU);
-    const int nt_dn = (p.L.H + 64 * PF_RG_DN - 1) / (64 * PF_RG_DN);
+    const int rows_gu = 4 * 16 * PF_RG_GU, rows_dn = 8 * 16 * PF_RG_DN;   // weight rows per workgroup
+    const int nt_gu = (Imax + rows_gu - 1) / rows_gu;
+    const int nt_dn = (p.L.H + rows_dn - 1) / rows_dn;
     hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(PF_THREADS), 0, s, p, nt_gu);
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(PF_THREADS), 0, s, p, nt_dn);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
+    hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
     hipLaunchKernelGGL(pf_combine_kernel, dim3(p.T), dim3(PF_THREADS), 0, s, p);
     return hipGetLastError();
 }
