@@ -15,6 +15,8 @@
 #include "rowdot.h"
 #include "stream.h"
 
+#include <type_traits>
+
 namespace moeq {
 
 constexpr int GEMV_L = 7;    // 16-byte loads per thread per chunk: 28 KiB stages
@@ -25,9 +27,15 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restric
                                                    const uint8_t *__restrict__ scales, int rows, int cols,
                                                    const uint16_t *__restrict__ x, int B, void *__restrict__ y,
                                                    int out_f32, int RC, int cpw) {
-    constexpr int L_ = GEMV_L, NS = GEMV_NS, STAGE = L_ * 4096;
+    constexpr int L_ = GEMV_L, STAGE = L_ * 4096;
+    static_assert(GEMV_NS == 4, "four stage objects");
     constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * STAGE];
+    // four stages as separate objects: the compiler can then tell a copy into
+    // one stage from reads of another and does not drain the pipeline
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring3[STAGE];
     __shared__ u32 s_pair[PAIR];
     __shared__ float s_scale[LUT_SCALE];
     const Luts Lt{s_pair, s_scale};
@@ -45,33 +53,50 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restric
     const int n = (c0 + cpw < NC ? c0 + cpw : NC) - c0;
     if (n <= 0) return;   // uniform over the workgroup
 
+    auto stage = [&](auto sc) -> uint8_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0) return ring0;
+        else if constexpr (S == 1) return ring1;
+        else if constexpr (S == 2) return ring2;
+        else return ring3;
+    };
+    auto src = [&](int i) {
+        const int r0 = (c0 + i) * RC;
+        const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
+        return chunk_src(rc, rs, r0, nr, (u32)crb, (u32)srb);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
     for (int t0 = 0; t0 < B; t0 += MT) {
         u32 xr[Q][MT][16];
         const uint16_t *xp[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) xp[t] = (t0 + t < B) ? x + (int64_t)(t0 + t) * cols : nullptr;
         load_x_units<Q, MT>(xr, xp, U, lr, LPR);
+        wait_vm<0>();   // x in registers before the ring starts
 
-        auto src = [&](int i) {
+        // chunks 0..2 in flight; chunk i lives in stage i % 4
+        issue_chunk<L_>(stage(I0{}), src(0), tid);
+        if (1 < n) issue_chunk<L_>(stage(I1{}), src(1), tid);
+        if (2 < n) issue_chunk<L_>(stage(I2{}), src(2), tid);
+
+        // Chunk i: wait for this thread's loads of it (loads retire in issue
+        // order; chunks i+1, i+2 may still be in flight), barrier (every
+        // thread's loads landed, and every wave finished chunk i-1, whose
+        // stage the copy of chunk i+3 then reuses), compute.
+        auto step = [&](auto dc, int i) {
+            constexpr int d = decltype(dc)::value;
+            if (i + 2 < n) wait_vm<2 * L_>();
+            else if (i + 1 < n) wait_vm<L_>();
+            else wait_vm<0>();
+            ring_barrier();
+            if (i + 3 < n) issue_chunk<L_>(stage(std::integral_constant<int, (d + 3) % 4>{}), src(i + 3), tid);
             const int r0 = (c0 + i) * RC;
             const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
-            return chunk_src(rc, rs, r0, nr, (u32)crb, (u32)srb);
-        };
-#pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-            if (i < n) issue_chunk<L_>(ring + i * STAGE, src(i), tid);
-
-        for (int i = 0; i < n; ++i) {
-            if (i + NS - 1 < n) {
-                issue_chunk<L_>(ring + ((i + NS - 1) % NS) * STAGE, src(i + NS - 1), tid);
-                wait_vm<(NS - 1) * L_>();
-            } else {
-                wait_vm<0>();
-            }
-            __syncthreads();
-            const int r0 = (c0 + i) * RC;
-            const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
-            const uint8_t *sc = ring + (i % NS) * STAGE;
+            const uint8_t *sc = stage(dc);
             const uint8_t *ss = sc + ((nr * crb + 1023) / 1024) * 1024 + ((r0 * srb) & 15);
             constexpr int R = 2;
             for (int base = w * RPW; base < nr; base += RING_WAVES * RPW * R) {
@@ -95,8 +120,14 @@ __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restric
                     }
                 }
             }
-            __syncthreads();
+        };
+        for (int i = 0; i < n; i += 4) {
+            step(I0{}, i);
+            if (i + 1 < n) step(I1{}, i + 1);
+            if (i + 2 < n) step(I2{}, i + 2);
+            if (i + 3 < n) step(I3{}, i + 3);
         }
+        ring_barrier();   // every wave is done with the ring before the next token pass refills it
     }
 }
 

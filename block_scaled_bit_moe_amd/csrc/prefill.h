@@ -261,8 +261,7 @@ __device__ inline void pf_barrier() {
 
 template <int N>
 __device__ inline void pf_wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    wait_vm<N>();
 }
 
 // Vector-memory loads of one weight unit.

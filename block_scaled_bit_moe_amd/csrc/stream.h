@@ -76,10 +76,27 @@ __device__ inline void issue_chunk(uint8_t *stage, const ChunkSrc &c, int tid) {
 }
 
 // Wait until this thread's loads of the chunk issued `behind` chunks ago
-// have landed (at most `behind` * L later loads still outstanding).
+// have landed (at most N loads still outstanding).  Emitted through the
+// builtin so that the compiler's own wait insertion knows which loads are
+// complete (an s_waitcnt in inline assembly is opaque to it); the clobber
+// keeps memory accesses on their side.  Encoding (gfx9): vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
 template <int N>
 __device__ inline void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for the ring.  __syncthreads() carries release/acquire
+// fences that make the compiler wait for every outstanding vector load
+// (vmcnt(0)), which would empty the ring at each chunk; callers wait for
+// exactly the chunk they need with wait_vm first.  The memory clobbers keep
+// LDS accesses on their side of the barrier.
+__device__ inline void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Rows that fit in one stage of L * 4 KiB.
@@ -94,19 +111,72 @@ __host__ __device__ inline int rows_per_chunk(int L, int crb, int srb) {
     return rc;
 }
 
-// One unit of row r of a chunk held in LDS (codes at `codes`, scales at `scales`).
+// LDS reads of the ring in inline assembly.  The compiler cannot always tell
+// which stage a pointer inside a loop refers to, and then waits for every
+// outstanding buffer-to-LDS copy before each LDS read (vmcnt(0)), which
+// empties the ring.  These reads are invisible to that analysis; the
+// workgroup barrier after wait_vm already guarantees the chunk has landed,
+// and lds_fence() waits for the reads themselves.
+typedef __attribute__((ext_vector_type(4))) u32 lds_u32x4;
+typedef __attribute__((ext_vector_type(2))) u32 lds_u32x2;
+__device__ inline u32 lds_addr(const void *p) {
+    return (u32)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ inline lds_u32x4 ds_b128(u32 a) {
+    lds_u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+__device__ inline lds_u32x2 ds_b64(u32 a) {
+    lds_u32x2 v;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+__device__ inline u32 ds_u8(u32 a) {
+    u32 v;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+
+// One unit of row r of a chunk held in LDS (codes at `codes`, scales at
+// `scales`), read with the assembly loads above: the values are valid only
+// after lds_settle().
+template <int FMT> struct LdsUnit;
+template <> struct LdsUnit<FMT_E2M1> { lds_u32x4 c; u32 s0, s1; };
+template <> struct LdsUnit<FMT_E2M3> { lds_u32x2 c0, c1, c2; u32 s; };
+
 template <int FMT>
-__device__ inline void lds_unit(Unit<FMT> &U, const uint8_t *codes, const uint8_t *scales, int r, int crb, int srb,
-                                int u) {
+__device__ inline void lds_unit_issue(LdsUnit<FMT> &V, const uint8_t *codes, const uint8_t *scales, int r, int crb,
+                                      int srb, int u) {
     if constexpr (FMT == FMT_E2M1) {
-        U.c = *reinterpret_cast<const uint4 *>(codes + r * crb + 16 * u);
-        U.s = *reinterpret_cast<const uint16_t *>(scales + r * srb + 2 * u);
+        V.c = ds_b128(lds_addr(codes + r * crb + 16 * u));
+        const u32 sa = lds_addr(scales + r * srb + 2 * u);   // any byte alignment
+        V.s0 = ds_u8(sa);
+        V.s1 = ds_u8(sa + 1);
     } else {
-        const uint8_t *p = codes + r * crb + 24 * u;
-        U.c0 = *reinterpret_cast<const uint2 *>(p);
-        U.c1 = *reinterpret_cast<const uint2 *>(p + 8);
-        U.c2 = *reinterpret_cast<const uint2 *>(p + 16);
-        U.s = scales[r * srb + (u >> 2)];
+        const u32 p = lds_addr(codes + r * crb + 24 * u);
+        V.c0 = ds_b64(p);
+        V.c1 = ds_b64(p + 8);
+        V.c2 = ds_b64(p + 16);
+        V.s = ds_u8(lds_addr(scales + r * srb + (u >> 2)));
+    }
+}
+
+// Wait for the issued reads, and make every later use of their registers
+// depend on that wait.
+__device__ inline void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <int FMT>
+__device__ inline void lds_settle(LdsUnit<FMT> &V, Unit<FMT> &U) {
+    if constexpr (FMT == FMT_E2M1) {
+        asm volatile("" : "+v"(V.c), "+v"(V.s0), "+v"(V.s1));
+        U.c = make_uint4(V.c[0], V.c[1], V.c[2], V.c[3]);
+        U.s = V.s0 | (V.s1 << 8);
+    } else {
+        asm volatile("" : "+v"(V.c0), "+v"(V.c1), "+v"(V.c2), "+v"(V.s));
+        U.c0 = make_uint2(V.c0[0], V.c0[1]);
+        U.c1 = make_uint2(V.c1[0], V.c1[1]);
+        U.c2 = make_uint2(V.c2[0], V.c2[1]);
+        U.s = V.s;
     }
 }
 
@@ -117,13 +187,20 @@ __device__ inline void rows_dot_lds(const uint8_t *codes, const uint8_t *scales,
                                     int U, int lr, int LPR, const u32 (&xh)[Q][MT][16], const u32 (&xl)[Q][MT][16],
                                     const Luts &L, float (&acc)[R][MT]) {
     Unit<FMT> un[R][Q];
+    LdsUnit<FMT> lv[R][Q];
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int u = lr + LPR * q;
-            if (u < U && row[b] >= 0) lds_unit<FMT>(un[b][q], codes, scales, row[b], crb, srb, u);
+            // rows past the chunk and units past the row read a valid address; their result is unused
+            lds_unit_issue<FMT>(lv[b][q], codes, scales, row[b] >= 0 ? row[b] : 0, crb, srb, u < U ? u : 0);
         }
+    lds_wait();
+#pragma unroll
+    for (int b = 0; b < R; ++b)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) lds_settle<FMT>(lv[b][q], un[b][q]);
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
