@@ -14,6 +14,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -276,8 +277,8 @@ __device__ inline float group_sum_dpp(float v, int G) {
 
 // ----------------------------------------------------------------------------
 // Routing helpers.  Order key of an fp32 logit: a larger float gets a larger
-// key, +0 and -0 get the same key, NaN gets 1 (below every number) and 0 marks
-// an entry already taken.
+// key, +0 and -0 get the same key, NaN gets 1 (below every number); 0 is left
+// for "no expert".
 __device__ inline u32 logit_key(float f) {
     u32 b = __builtin_bit_cast(u32, f);
     if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 1u;   // NaN
@@ -296,77 +297,107 @@ __device__ inline u32 dpp_u32(u32 old, u32 v) {
     return (u32)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, false);
 }
 
-// max (or min) over the 64 lanes, returned uniform
+// max over the 64 lanes, returned uniform: four in-row DPP stages
+// (each lane's source is always valid, so the move folds into the max), then
+// the four row results combined on the scalar unit
+template <int CTRL>
+__device__ inline u32 dpp_mov_u32(u32 v) {
+    return (u32)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
 __device__ inline u32 wave_max_u32(u32 v) {
-    v = max(v, dpp_u32<0xB1>(v, v));          // quad_perm [1,0,3,2]
-    v = max(v, dpp_u32<0x4E>(v, v));          // quad_perm [2,3,0,1]
-    v = max(v, dpp_u32<0x141>(v, v));         // row_half_mirror
-    v = max(v, dpp_u32<0x140>(v, v));         // row_mirror
-    v = max(v, dpp_u32<0x142, 0xA>(v, v));    // row_bcast:15 into rows 1, 3
-    v = max(v, dpp_u32<0x143, 0xC>(v, v));    // row_bcast:31 into rows 2, 3
-    return (u32)__builtin_amdgcn_readlane((int)v, 63);
+    v = max(v, dpp_mov_u32<0xB1>(v));         // quad_perm [1,0,3,2]
+    v = max(v, dpp_mov_u32<0x4E>(v));         // quad_perm [2,3,0,1]
+    v = max(v, dpp_mov_u32<0x141>(v));        // row_half_mirror
+    v = max(v, dpp_mov_u32<0x140>(v));        // row_mirror
+    const u32 r0 = (u32)__builtin_amdgcn_readlane((int)v, 0);
+    const u32 r1 = (u32)__builtin_amdgcn_readlane((int)v, 16);
+    const u32 r2 = (u32)__builtin_amdgcn_readlane((int)v, 32);
+    const u32 r3 = (u32)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
-__device__ inline u32 wave_min_u32(u32 v) {
-    v = min(v, dpp_u32<0xB1>(v, v));
-    v = min(v, dpp_u32<0x4E>(v, v));
-    v = min(v, dpp_u32<0x141>(v, v));
-    v = min(v, dpp_u32<0x140>(v, v));
-    v = min(v, dpp_u32<0x142, 0xA>(v, v));
-    v = min(v, dpp_u32<0x143, 0xC>(v, v));
-    return (u32)__builtin_amdgcn_readlane((int)v, 63);
-}
 
 // One wave routes one token: the k best experts in rank order and their
 // softmax weights over the k picks (Strata docs/INTEL.md, "The engine itself on
-// Intel": router_top10, for any k).  Expert e sits in lane e % 64, slot e / 64,
-// so among equal keys the lowest slot and then the lowest lane is the lowest
-// index.  Each of the k rounds takes the wave maximum of the lanes' best keys
-// (DPP); a single lane holding it wins outright (the usual case), otherwise the
-// lowest index among the holders is found with a wave minimum.  Lanes
-// 0 .. k-1 end with (idx, w) of rank = lane; other lanes return idx -1.
+// Intel": router_top10, for any k).
+//
+// Every expert gets a unique 64-bit key: the order key of its logit in the
+// high half and the complement of its index in the low half, so a larger key
+// means a larger logit, or the same logit and a lower index — the ranking
+// rule itself, with no tie left to break.  Lane l holds experts
+// l*PER_LANE .. l*PER_LANE + PER_LANE - 1 (contiguous loads) and sorts its keys
+// once (bitonic network, descending).  Each of the k rounds takes the wave
+// maximum of the lanes' first keys (two 32-bit DPP maxima: the logit half,
+// then the index half among the holders of that logit); the lane whose first
+// key it is drops it.  The winner's index is in the key itself.  Lanes 0 .. k-1 end with
+// (idx, w) of rank = lane; other lanes return idx -1.
 template <int PER_LANE>
-__device__ inline void route_one_token_wave(const float *__restrict__ logits, int E, int k, int lane,
-                                            int &my_idx, float &my_w) {
-    u32 key[PER_LANE];
+__device__ inline void route_load_logits(const float *__restrict__ logits, int E, int lane, float (&lg)[PER_LANE]) {
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) lg[j] = logits[min(lane * PER_LANE + j, E - 1)];   // all loads in flight
+}
+
+template <int PER_LANE>
+__device__ inline void route_from_logits(const float (&lg)[PER_LANE], int E, int k, int lane, int &my_idx,
+                                         float &my_w) {
+    uint64_t key[PER_LANE];
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
-        const int e = j * WAVE + lane;
-        key[j] = (e < E) ? logit_key(logits[e]) : 0u;
+        const int e = lane * PER_LANE + j;
+        const u32 lk = (e < E) ? logit_key(lg[j]) : 0u;   // 0: no expert, below NaN (1)
+        key[j] = ((uint64_t)lk << 32) | (u32)~(u32)e;
     }
+    // bitonic sort, descending
+#pragma unroll
+    for (int sz = 2; sz <= PER_LANE; sz <<= 1)
+#pragma unroll
+        for (int j = sz >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const bool desc = (i & sz) == 0;
+                    const bool sw = desc ? (key[l] > key[i]) : (key[l] < key[i]);
+                    const uint64_t a = key[i], b = key[l];
+                    key[i] = sw ? b : a;
+                    key[l] = sw ? a : b;
+                }
+            }
     my_idx = -1;
     float my_l = 0.f, l0 = 0.f;
     for (int r = 0; r < k; ++r) {
-        // lane's best key and the lowest slot holding it
-        u32 best = key[0];
-        int bj = 0;
+        // the largest first key: its logit half first, then (among the lanes
+        // holding that logit, if more than one) its index half
+        const u32 hv = (u32)(key[0] >> 32), hl = (u32)key[0];
+        const u32 mv = wave_max_u32(hv);
+        const uint64_t holders = __ballot(hv == mv);
+        u32 ml;
+        if (__popcll(holders) == 1)      // the usual case: one lane holds that logit
+            ml = (u32)__builtin_amdgcn_readlane((int)hl, __ffsll((long long)holders) - 1);
+        else
+            ml = wave_max_u32(hv == mv ? hl : 0u);
+        const bool win = hv == mv && hl == ml;
 #pragma unroll
-        for (int j = 1; j < PER_LANE; ++j) {
-            const bool gt = key[j] > best;
-            best = gt ? key[j] : best;
-            bj = gt ? j : bj;
-        }
-        const u32 m = wave_max_u32(best);
-        const uint64_t holders = __ballot(best == m);
-        int e;
-        if (__popcll(holders) == 1) {
-            const int wl = __ffsll((long long)holders) - 1;
-            e = __builtin_amdgcn_readlane(bj, wl) * WAVE + wl;
-        } else {
-            e = (int)wave_min_u32(best == m ? (u32)(bj * WAVE + lane) : 0xFFFFFFFFu);
-        }
-        const int wj = e / WAVE, wl = e % WAVE;
-#pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) key[j] = (lane == wl && j == wj) ? 0u : key[j];
-        const float lv = logit_of_key(m);
+        for (int j = 0; j + 1 < PER_LANE; ++j) key[j] = win ? key[j + 1] : key[j];
+        if (win) key[PER_LANE - 1] = 0u;
+        const int e = (int)~ml;
+        const float lv = logit_of_key(mv);
         if (r == 0) l0 = lv;
         if (lane == r) { my_idx = e; my_l = lv; }
     }
     // weights: exp(l_r - l_0) / sum over the k picks (fp32, fixed order r = 0..k-1)
     const float ex = (lane < k) ? expf(my_l - l0) : 0.f;
     float z = 0.f;
-    for (int r = 0; r < k; ++r) z += __shfl(ex, r, WAVE);
+    for (int r = 0; r < k; ++r) z += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), r));
     my_w = (lane < k) ? ex / z : 0.f;
+}
+
+template <int PER_LANE>
+__device__ inline void route_one_token_wave(const float *__restrict__ logits, int E, int k, int lane, int &my_idx,
+                                            float &my_w) {
+    float lg[PER_LANE];
+    route_load_logits<PER_LANE>(logits, E, lane, lg);
+    route_from_logits<PER_LANE>(lg, E, k, lane, my_idx, my_w);
 }
 
 __device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }

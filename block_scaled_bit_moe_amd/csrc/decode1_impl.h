@@ -40,6 +40,7 @@ struct D1Plan {
     int g_gu;          // workgroups with gate/up work
     int rw;            // output rows per workgroup
     u32 magic_rw;      // floor((2^32-1) / rw) + 1: d / rw == umulhi(d, magic_rw) for the small d used here
+    int lpr_d;         // lanes per row of the down projection (down_lanes_per_row)
 };
 
 constexpr int D1_MAX_GROUPS = 33;           // k <= 32 routed + shared
@@ -77,9 +78,21 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     uint64_t *hw = reinterpret_cast<uint64_t *>(a.ws + d1_h_offset(H, I, Ish));
     const int64_t crbH = Fmt<FMT>::code_row_bytes(H), srbH = Fmt<FMT>::scale_row_bytes(H);
 
-    // call tag, activation units and the routing logits are all fetched at once
-    if (tid == 0) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
-    build_luts<FMT>(Lt, tid, 256, DEC == DEC_LUT);
+    // call tag, activation units and the routing logits are all fetched at once;
+    // the routing wave issues its logit loads first of all
+    float lgt[16];
+    if (wv == 0) {
+        if (E <= 64) route_load_logits<1>(a.logits, E, lane, reinterpret_cast<float(&)[1]>(lgt));
+        else if (E <= 128) route_load_logits<2>(a.logits, E, lane, reinterpret_cast<float(&)[2]>(lgt));
+        else if (E <= 256) route_load_logits<4>(a.logits, E, lane, reinterpret_cast<float(&)[4]>(lgt));
+        else if (E <= 512) route_load_logits<8>(a.logits, E, lane, reinterpret_cast<float(&)[8]>(lgt));
+        else route_load_logits<16>(a.logits, E, lane, lgt);
+    }
+    // the routing wave does nothing else until it has routed: the call tag and
+    // the tables come from the other three waves (first used after the
+    // barrier that follows routing)
+    if (tid == 64) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
+    if (wv > 0) build_luts<FMT>(Lt, tid - 64, 192, DEC == DEC_LUT);
     const int UH = H / 32, LPRg = lanes_per_row(UH), RPWg = WAVE / LPRg;
     const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
     u32 xr[QG][1][16];
@@ -124,11 +137,11 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     if (wv == 0) {
         int e;
         float wt;
-        if (E <= 64) route_one_token_wave<1>(a.logits, E, k, lane, e, wt);
-        else if (E <= 128) route_one_token_wave<2>(a.logits, E, k, lane, e, wt);
-        else if (E <= 256) route_one_token_wave<4>(a.logits, E, k, lane, e, wt);
-        else if (E <= 512) route_one_token_wave<8>(a.logits, E, k, lane, e, wt);
-        else route_one_token_wave<16>(a.logits, E, k, lane, e, wt);
+        if (E <= 64) route_from_logits<1>(reinterpret_cast<const float(&)[1]>(lgt), E, k, lane, e, wt);
+        else if (E <= 128) route_from_logits<2>(reinterpret_cast<const float(&)[2]>(lgt), E, k, lane, e, wt);
+        else if (E <= 256) route_from_logits<4>(reinterpret_cast<const float(&)[4]>(lgt), E, k, lane, e, wt);
+        else if (E <= 512) route_from_logits<8>(reinterpret_cast<const float(&)[8]>(lgt), E, k, lane, e, wt);
+        else route_from_logits<16>(lgt, E, k, lane, e, wt);
         if (lane < k) {
             S.sel[lane] = e;
             S.wsel[lane] = wt;
@@ -145,27 +158,32 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     __syncthreads();
 
     // ------------------------------------------------ issue the remaining weight loads
-    if (has_gu && !gu_shared) {
-        const int e = S.sel[gu_group];
-        issue_gu(ly.w13c + (int64_t)e * 2 * I * crbH, ly.w13s + (int64_t)e * 2 * I * srbH);
-    }
-    // down task d in [0, NG*nr): group d / rw, local row d % rw
+    // Every expert id needed is read from LDS first, then the gate/up and the
+    // down loads are issued back to back (nothing in between that would make
+    // the compiler wait for the first batch before issuing the second).
     const int o0 = w * plan.rw;
     const int nr = max(0, min(H, o0 + plan.rw) - o0);
-    const int LPRd = down_lanes_per_row(I, Ish), RPWd = WAVE / LPRd;
+    const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
     const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
-    Unit<FMT> dn_un[MD][QD];
-    int dn_g[MD], dn_r[MD];
+    int dn_g[MD], dn_r[MD], dn_e[MD];
 #pragma unroll
     for (int s = 0; s < MD; ++s) {
+        // down task d in [0, NG*nr): group d / rw, local row d % rw
         const int d = (wv + 4 * s) * RPWd + rsd;
         const int g = (int)__umulhi((u32)d, plan.magic_rw);
         const int r = d - g * plan.rw;
         const bool ok = (nr > 0) && (g < NG) && (r < nr);
         dn_g[s] = ok ? g : -1;
         dn_r[s] = r;
-        if (ok) {
-            const int e = S.sel[g];
+        dn_e[s] = ok ? S.sel[g] : 0;
+    }
+    const int gu_e = (has_gu && !gu_shared) ? S.sel[gu_group] : 0;
+    if (has_gu && !gu_shared) issue_gu(ly.w13c + (int64_t)gu_e * 2 * I * crbH, ly.w13s + (int64_t)gu_e * 2 * I * srbH);
+    Unit<FMT> dn_un[MD][QD];
+#pragma unroll
+    for (int s = 0; s < MD; ++s) {
+        if (dn_g[s] >= 0) {
+            const int e = dn_e[s], r = dn_r[s];
             const int Ig = (e >= 0) ? I : Ish;
             const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
             const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o0 + r) * crbI : ly.sh2c + (int64_t)(o0 + r) * crbI;
@@ -209,9 +227,10 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
 
     // ------------------------------------------------ gather all of h (poll until every tag is current)
     // into LDS as bf16 hi/lo words: per group, unit u = 16 words of hi pairs then 16 words of lo pairs.
-    // Batches of NB 16-byte pieces (2 elements each) per thread, every batch loaded at once.
+    // Batches of NB 16-byte pieces (2 elements each) per thread, every batch loaded at once (each
+    // batch costs a device-coherent round trip, so a batch covers a whole layer of the common sizes).
     {
-        constexpr int NB = 8;
+        constexpr int NB = 12;   // 3,072 pieces per batch: one round trip for 11 groups of 512
         const int total2 = NG * Imax / 2;
         const __amdgpu_buffer_rsrc_t hr =
             __builtin_amdgcn_make_buffer_rsrc(hw, (short)0, (int)(NG * Imax * 8), 0x00020000);
@@ -352,7 +371,7 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
         if (NG * rw > 4 * MD * RPWd) continue;
         // every workgroup must publish h (see the tag argument above): no down-only workgroups
         if ((L.H + rw - 1) / rw > g_gu) continue;
-        D1Plan plan{pp, g_gu, rw, (u32)(0xFFFFFFFFull / (u32)rw + 1u)};
+        D1Plan plan{pp, g_gu, rw, (u32)(0xFFFFFFFFull / (u32)rw + 1u), down_lanes_per_row(L.I, L.Ish)};
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), dyn, s, a, plan);
         return hipGetLastError();
     }

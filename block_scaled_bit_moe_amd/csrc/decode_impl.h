@@ -249,7 +249,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int64_t crbH = Fmt<FMT>::code_row_bytes(H), srbH = Fmt<FMT>::scale_row_bytes(H);
     const int UH = H / 32, LPRg = lanes_per_row(UH), RPWg = WAVE / LPRg;
     const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
-    const int gu_per_routed = I / DEC_S1, gu_shared = Ish / DEC_S1;
+    constexpr int S1 = DEC_S1;
+    const int gu_per_routed = I / S1, gu_shared = Ish / S1;
     const int n_gu = NRG * gu_per_routed + (NG - NRG) * gu_shared;
     const int n_slices = (H + DEC_S2 - 1) / DEC_S2;
     const int total = n_gu + n_slices * NG;
@@ -273,37 +274,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 for (int j = 0; j < MT; ++j)
                     xp[j] = (tt + j < mg) ? a.x + (int64_t)S.p_tok[pos0 + tt + j] * H : nullptr;
                 load_x_units<QG, MT>(xr, xp, UH, lrg, LPRg);
+                // rows v of the item (gate rows 0..S1-1, up rows S1..2*S1-1), streamed R per pass
                 constexpr int R = 2;
-                for (int v0 = wv * RPWg; v0 < 2 * DEC_S1; v0 += 4 * RPWg * R) {
-                    const uint8_t *crow[R], *srow[R];
-                    int vr[R];
+                const int npass = (2 * S1 + 4 * RPWg * R - 1) / (4 * RPWg * R);
+                auto row = [&](int p, int b, const uint8_t *&c, const uint8_t *&sc) -> int {
+                    const int v = p * 4 * RPWg * R + wv * RPWg + b * 4 * RPWg + rsg;
+                    const int vv = v < 2 * S1 ? v : 0;
+                    const int r = vv < S1 ? s * S1 + vv : Ig + s * S1 + (vv - S1);
+                    c = c13 + (int64_t)r * crbH;
+                    sc = s13 + (int64_t)r * srbH;
+                    return v < 2 * S1 ? v : -1;
+                };
+                auto out = [&](int, int, int v, const float (&acc)[MT]) {
+                    if (v >= 0 && lrg == 0)
 #pragma unroll
-                    for (int b = 0; b < R; ++b) {
-                        vr[b] = v0 + b * 4 * RPWg + rsg;
-                        const int vv = vr[b] < 2 * DEC_S1 ? vr[b] : 0;
-                        const int row = vv < DEC_S1 ? s * DEC_S1 + vv : Ig + s * DEC_S1 + (vv - DEC_S1);
-                        crow[b] = c13 + (int64_t)row * crbH;
-                        srow[b] = s13 + (int64_t)row * srbH;
-                    }
-                    float acc[R][MT];
-                    rows_dot<FMT, DEC, QG, MT, R, false>(crow, srow, UH, lrg, LPRg, xr, xr, L, acc);
-#pragma unroll
-                    for (int b = 0; b < R; ++b)
-                        if (vr[b] < 2 * DEC_S1 && lrg == 0)
-#pragma unroll
-                            for (int j = 0; j < MT; ++j) S.gu[vr[b]][j] = acc[b][j];
-                }
+                        for (int j = 0; j < MT; ++j) S.gu[v][j] = acc[j];
+                };
+                RowPipe<FMT, DEC, QG, MT, R, false> pipe;
+                pipe.begin(row, UH, lrg, LPRg);
+                pipe.run(npass, row, UH, lrg, LPRg, xr, xr, L, out);
                 __syncthreads();
-                for (int q = tid; q < (DEC_S1 / 2) * MT; q += 256) {
+                for (int q = tid; q < (S1 / 2) * MT; q += 256) {
                     const int kp = q / MT, j = q % MT;
                     if (tt + j < mg) {
                         const int i0 = 2 * kp;
-                        const float h0 = silu_f32(S.gu[i0][j]) * S.gu[DEC_S1 + i0][j];
-                        const float h1 = silu_f32(S.gu[i0 + 1][j]) * S.gu[DEC_S1 + i0 + 1][j];
+                        const float h0 = silu_f32(S.gu[i0][j]) * S.gu[S1 + i0][j];
+                        const float h1 = silu_f32(S.gu[i0 + 1][j]) * S.gu[S1 + i0 + 1][j];
                         const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
                         const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
                         const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-                        const int p = (s * DEC_S1 + i0) >> 1, uu = p >> 4, kk2 = p & 15;
+                        const int p = (s * S1 + i0) >> 1, uu = p >> 4, kk2 = p & 15;
                         u32 *row = hl + (size_t)(pos0 + tt + j) * Imax + 32 * uu;
                         st_relaxed_agent(row + kk2, hi0 | (hi1 << 16));
                         st_relaxed_agent(row + 16 + kk2, lo0 | (lo1 << 16));
@@ -320,7 +320,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const int j = d / NG, g = d % NG;
             const int e = S.g_expert[g];
             const int Ig = (e >= 0) ? I : Ish;
-            const u32 need = (u32)(Ig / DEC_S1);
+            const u32 need = (u32)(Ig / S1);
+            const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
+            const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)e * H * crbI : ly.sh2c;
+            const uint8_t *s2 = (e >= 0) ? ly.w2s + (int64_t)e * H * srbI : ly.sh2s;
+            const int UI = Ig / 32, LPRd = down_lanes_per_row(I, Ish), RPWd = WAVE / LPRd;
+            const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
+            const int mg = S.g_count[g], pos0 = S.g_start[g];
+            const int o_lo = j * DEC_S2, o_hi = (o_lo + DEC_S2 < H) ? o_lo + DEC_S2 : H;
+            // output rows o of the slice, streamed R per pass
+            constexpr int R = 2;
+            const int npass = (o_hi - o_lo + 4 * RPWd * R - 1) / (4 * RPWd * R);
+            auto row = [&](int p, int b, const uint8_t *&c, const uint8_t *&sc) -> int {
+                const int o = o_lo + p * 4 * RPWd * R + wv * RPWd + b * 4 * RPWd + rsd;
+                const int oo = o < o_hi ? o : o_lo;
+                c = c2 + (int64_t)oo * crbI;
+                sc = s2 + (int64_t)oo * srbI;
+                return o < o_hi ? o : -1;
+            };
+            RowPipe<FMT, DEC, QD, MT, R, true> pipe;
+            pipe.begin(row, UI, lrd, LPRd);   // the weights do not depend on h: in flight during the wait
             if (tid == 0) {
                 // bounded wait; spin_limit 0 (the test hook) expires at once without polling
                 u32 spins = 0;
@@ -330,41 +349,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 }
             }
             __syncthreads();
-            const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
-            const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)e * H * crbI : ly.sh2c;
-            const uint8_t *s2 = (e >= 0) ? ly.w2s + (int64_t)e * H * srbI : ly.sh2s;
-            const int UI = Ig / 32, LPRd = down_lanes_per_row(I, Ish), RPWd = WAVE / LPRd;
-            const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
-            const int mg = S.g_count[g], pos0 = S.g_start[g];
-            const int o_lo = j * DEC_S2, o_hi = (o_lo + DEC_S2 < H) ? o_lo + DEC_S2 : H;
             for (int tt = 0; tt < mg; tt += MT) {
                 u32 xh[QD][MT][16], xl[QD][MT][16];
                 int pp[MT];
 #pragma unroll
                 for (int jj = 0; jj < MT; ++jj) pp[jj] = (tt + jj < mg) ? pos0 + tt + jj : -1;
                 load_h_units<QD, MT>(xh, xl, hl_rsrc, pp, Imax, UI, lrd, LPRd);
-                constexpr int R = 2;
-                for (int o0 = o_lo + wv * RPWd; o0 < o_hi; o0 += 4 * RPWd * R) {
-                    const uint8_t *crow[R], *srow[R];
-                    int orow[R];
+                auto out = [&](int, int, int o, const float (&acc)[MT]) {
+                    if (o >= 0 && lrd == 0)
 #pragma unroll
-                    for (int b = 0; b < R; ++b) {
-                        orow[b] = o0 + b * 4 * RPWd + rsd;
-                        const int oo = orow[b] < o_hi ? orow[b] : o_lo;
-                        crow[b] = c2 + (int64_t)oo * crbI;
-                        srow[b] = s2 + (int64_t)oo * srbI;
-                    }
-                    float acc[R][MT];
-                    rows_dot<FMT, DEC, QD, MT, R, true>(crow, srow, UI, lrd, LPRd, xh, xl, L, acc);
-#pragma unroll
-                    for (int b = 0; b < R; ++b)
-                        if (orow[b] < o_hi && lrd == 0)
-#pragma unroll
-                            for (int jj = 0; jj < MT; ++jj)
-                                if (tt + jj < mg)
-                                    st_relaxed_agent(ybuf + (size_t)(pos0 + tt + jj) * H + orow[b],
-                                                     __builtin_bit_cast(u32, acc[b][jj]));
-                }
+                        for (int jj = 0; jj < MT; ++jj)
+                            if (tt + jj < mg)
+                                st_relaxed_agent(ybuf + (size_t)(pos0 + tt + jj) * H + o, __builtin_bit_cast(u32, acc[jj]));
+                };
+                if (tt > 0) pipe.begin(row, UI, lrd, LPRd);
+                pipe.run(npass, row, UI, lrd, LPRd, xh, xl, L, out);
             }
             wait_stores();
             __syncthreads();
