@@ -21,6 +21,7 @@ namespace moeq {
 
 constexpr int GEMV_L = 7;    // 16-byte loads per thread per chunk: 28 KiB stages
 constexpr int GEMV_NS = 4;   // stages in flight
+constexpr int GEMV_REG_WG_PER_CU = 2;   // one-token kernel: workgroups per CU (its occupancy)
 
 template <int FMT, int DEC, int Q, int MT>
 __global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restrict__ codes,
@@ -156,9 +157,11 @@ static hipError_t gemv_ring_go(const uint8_t *codes, const uint8_t *scales, int 
     return hipGetLastError();
 }
 
-// Register-pipelined variant: the x units stay in VGPRs and every wave keeps
-// R rows of loads in flight.  Used for one token, where it streams faster
-// than the ring (fewer VGPRs for x, more waves per CU).
+// Register-streamed variant: the x units stay in VGPRs, and each wave walks
+// its rows (every nw-th row group) R per pass with the next pass's loads in
+// flight (RowPipe).  A grid of a few workgroups per CU, so every wave streams
+// many rows after loading x once.  Used for one token, where it streams
+// faster than the ring (fewer VGPRs for x, more waves per CU).
 template <int FMT, int DEC, int Q, int MT, int R>
 __global__ __launch_bounds__(256) void gemv_reg_kernel(const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, int rows, int cols,
@@ -178,6 +181,8 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(const uint8_t *__restrict
     const int nw = gridDim.x * (blockDim.x / WAVE);
     const int gw = blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x >> 6);
     const int ngroups = (rows + RPW - 1) / RPW;
+    if (gw >= ngroups) return;   // uniform over the wave; no barrier follows
+    const int npass = (ngroups - gw + nw * R - 1) / (nw * R);
 
     for (int t0 = 0; t0 < B; t0 += MT) {
         u32 xr[Q][MT][16];
@@ -186,33 +191,29 @@ __global__ __launch_bounds__(256) void gemv_reg_kernel(const uint8_t *__restrict
         for (int t = 0; t < MT; ++t) xp[t] = (t0 + t < B) ? x + (int64_t)(t0 + t) * cols : nullptr;
         load_x_units<Q, MT>(xr, xp, U, lr, LPR);
 
-        for (int g0 = gw; g0 < ngroups; g0 += nw * R) {
-            const uint8_t *crow[R], *srow[R];
-            int row[R];
-            bool valid[R];
+        // pass p, slot b: row group gw + (p * R + b) * nw (past the end: row 0, result dropped)
+        auto row = [&](int p, int b, const uint8_t *&c, const uint8_t *&sc) -> int {
+            const int grp = gw + (p * R + b) * nw;
+            const int r = grp * RPW + rsub;
+            const bool ok = grp < ngroups && r < rows;
+            const int rr = ok ? r : 0;
+            c = codes + (int64_t)rr * crb;
+            sc = scales + (int64_t)rr * srb;
+            return ok ? r : -1;
+        };
+        auto out = [&](int, int, int r, const float (&acc)[MT]) {
+            if (r < 0 || lr != 0) return;
 #pragma unroll
-            for (int b = 0; b < R; ++b) {
-                const int grp = g0 + b * nw;
-                row[b] = grp * RPW + rsub;
-                valid[b] = (grp < ngroups) && (row[b] < rows);
-                const int rr = valid[b] ? row[b] : 0;
-                crow[b] = codes + (int64_t)rr * crb;
-                srow[b] = scales + (int64_t)rr * srb;
+            for (int t = 0; t < MT; ++t) {
+                if (t0 + t >= B) continue;
+                const int64_t o = (int64_t)(t0 + t) * rows + r;
+                if (out_f32) reinterpret_cast<float *>(y)[o] = acc[t];
+                else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(acc[t]);
             }
-            float acc[R][MT];
-            rows_dot<FMT, DEC, Q, MT, R, false>(crow, srow, U, lr, LPR, xr, xr, L, acc);
-#pragma unroll
-            for (int b = 0; b < R; ++b) {
-                if (!valid[b] || lr != 0) continue;
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    if (t0 + t >= B) continue;
-                    const int64_t o = (int64_t)(t0 + t) * rows + row[b];
-                    if (out_f32) reinterpret_cast<float *>(y)[o] = acc[b][t];
-                    else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(acc[b][t]);
-                }
-            }
-        }
+        };
+        RowPipe<FMT, DEC, Q, MT, R, false> pipe;
+        pipe.begin(row, U, lr, LPR);
+        pipe.run(npass, row, U, lr, LPR, xr, xr, L, out);
     }
 }
 
@@ -222,8 +223,10 @@ static hipError_t gemv_reg_go(const uint8_t *codes, const uint8_t *scales, int r
     constexpr int R = 2;
     const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
     const int ngroups = (rows + RPW - 1) / RPW;
+    // enough waves to fill the CUs, each with several passes to stream
     int blocks = (ngroups + 4 * R - 1) / (4 * R);
-    if (blocks > 256 * 16) blocks = 256 * 16;
+    const int cap = num_cus() * GEMV_REG_WG_PER_CU;
+    if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL((gemv_reg_kernel<FMT, DEC, Q, MT, R>), dim3(blocks), dim3(256), 0, s, codes, scales, rows, cols, x,
                        B, y, out_f32);
     return hipGetLastError();
