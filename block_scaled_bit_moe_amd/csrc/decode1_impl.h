@@ -4,42 +4,59 @@
 //
 // With one token every selected expert serves exactly one row, so the work is
 // static once the token is routed:
-//   gate | up : workgroup w < G_gu computes PP consecutive (gate row, up row)
-//               pairs of ONE expert (the shared expert's workgroups first, so
-//               they need not wait for the routing);
+//   gate | up : workgroup w computes PP consecutive (gate row, up row) pairs
+//               of ONE expert; the routed experts' workgroups come first and
+//               the shared expert's last;
 //   down      : workgroup w computes RW consecutive output rows for EVERY
 //               selected expert and combines them itself, in rank order, so no
 //               partial sums leave the CU.
 // Each workgroup routes the token itself, then issues all of its weight loads
-// at once (gate/up rows and down rows, into registers), so the whole layer is
-// in flight after one routing delay.
+// at once (gate/up rows, then down rows, into registers), so the whole layer
+// is in flight after one routing delay.  Every load is issued
+// unconditionally (idle slots re-load a row the workgroup loads anyway), so
+// the compiler counts outstanding loads exactly and the gate/up dots wait for
+// the gate/up rows only, not for the down rows behind them.
 //
-// The down rows need every expert's h.  Instead of a device-wide barrier, h is
-// published as 64-bit words (fp32 value, call tag) with atomic device-coherent
-// stores, and each consumer polls the words it needs until every tag is the
-// current one (bounded).  The tag is the workspace's call counter + 1: every
+// The down rows need every expert's h.  Wave 3 of each workgroup is its
+// exchange wave (it loads no down rows of its own): it stores the
+// workgroup's h as bf16 hi/lo pairs with device-coherent stores, waits for
+// them, then sets the workgroup's ready flag to the call tag.  It then polls
+// all flags (one 4-byte word per workgroup, so a poll costs little) and, as
+// soon as every producer of an expert group is ready, copies that group's h
+// straight from memory into LDS (buffer-load-to-LDS, no registers), until all
+// groups are in.  The tag is the workspace's call counter + 1: every
 // workgroup reads the counter on entry and raises it to counter + 1 on exit.
-// That is safe because every workgroup publishes some h (the grid has no
-// down-only workgroups), so none can finish before all have read the counter;
-// and it stays correct when the launch is replayed from a captured graph.
+// That is safe because every workgroup publishes h and none leaves before all
+// h is published, so none can finish before all have read the counter; and it
+// stays correct when the launch is replayed from a captured graph.
 #pragma once
 
 #include "kernels.h"
 #include "rowdot.h"
+#include "stream.h"
 
 namespace moeq {
 
 __device__ inline u32 d1_ld_relaxed(const u32 *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline void d1_st_relaxed(u32 *p, u32 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void d1_st64_relaxed(uint64_t *p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// OR over the 64 lanes, returned uniform (same DPP stages as wave_max_u32)
+__device__ inline u32 wave_or_u32(u32 v) {
+    v |= dpp_mov_u32<0xB1>(v);
+    v |= dpp_mov_u32<0x4E>(v);
+    v |= dpp_mov_u32<0x141>(v);
+    v |= dpp_mov_u32<0x140>(v);
+    return (u32)__builtin_amdgcn_readlane((int)v, 0) | (u32)__builtin_amdgcn_readlane((int)v, 16) |
+           (u32)__builtin_amdgcn_readlane((int)v, 32) | (u32)__builtin_amdgcn_readlane((int)v, 48);
 }
 
 struct D1Plan {
     int pp;            // gate/up pairs per workgroup (divides I and the shared I)
-    int g_gu;          // workgroups with gate/up work
+    int g_gu;          // workgroups; every one has gate/up work
+    int n_rt;          // workgroups of the routed experts (the first ones)
+    uint64_t magic_wpg;   // w / (I / pp) == (w * magic_wpg) >> 32 for w < g_gu
     int rw;            // output rows per workgroup
-    u32 magic_rw;      // floor((2^32-1) / rw) + 1: d / rw == umulhi(d, magic_rw) for the small d used here
+    uint64_t magic_rw;    // d / rw == (d * magic_rw) >> 32 for the small d used here
     int lpr_d;         // lanes per row of the down projection (down_lanes_per_row)
 };
 
@@ -55,11 +72,21 @@ struct D1Shared {
     float y[D1_MAX_GROUPS * D1_MAX_RW];   // down results: [group][local row]
 };
 
-// Region of the workspace holding h for this kernel: [group][Imax] 64-bit words.
-__host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
+// Regions of the workspace for this kernel: the ready flags (one u32 per
+// workgroup), then h as [group][Imax] u32 words in unit layout (unit u of 32
+// elements: 16 words of bf16 hi pairs, then 16 words of lo pairs).
+__host__ __device__ inline size_t d1_flag_offset(int H, int I, int Ish) {
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * 4 + (size_t)DEC_MAX_PAIRS * H * 4;
 }
+__host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
+    return d1_flag_offset(H, I, Ish) + (size_t)D1_MAX_WGS * 4;
+}
+
+// LDS layout of h: the 8 16-byte pieces of unit u are stored rotated by
+// (u >> 1) & 7, so the 16 lanes of a row reading units u .. u+15 at the same
+// piece hit 16 different bank groups.
+__device__ inline int d1_piece_swz(int u) { return (u >> 1) & 7; }
 
 template <int FMT, int DEC, int QG, int QD, int MG, int MD>
 __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan) {
@@ -69,13 +96,15 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     __shared__ D1Shared S;
     extern __shared__ __attribute__((aligned(16))) u32 s_h[];   // NG * Imax words
     const Luts Lt{s_pair, s_scale};
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const LayerArgs &ly = a.L;
     const int H = ly.H, I = ly.I, k = ly.k, Ish = ly.Ish, E = ly.E;
     const int NG = k + (Ish > 0 ? 1 : 0);
     const int Imax = I > Ish ? I : Ish;
     u32 *hdr = reinterpret_cast<u32 *>(a.ws);
-    uint64_t *hw = reinterpret_cast<uint64_t *>(a.ws + d1_h_offset(H, I, Ish));
+    u32 *flags = reinterpret_cast<u32 *>(a.ws + d1_flag_offset(H, I, Ish));
+    u32 *hp = reinterpret_cast<u32 *>(a.ws + d1_h_offset(H, I, Ish));
     const int64_t crbH = Fmt<FMT>::code_row_bytes(H), srbH = Fmt<FMT>::scale_row_bytes(H);
 
     // call tag, activation units and the routing logits are all fetched at once;
@@ -103,35 +132,34 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
 
     // ------------------------------------------------ gate/up share: group, first pair
     const int w = blockIdx.x;
-    const int sh_wgs = Ish / plan.pp;                 // shared expert's workgroups come first
-    const bool has_gu = w < plan.g_gu;
-    const bool gu_shared = has_gu && w < sh_wgs;
-    const int gu_group = !has_gu ? 0 : (gu_shared ? k : (w - sh_wgs) / (I / plan.pp));
-    const int gu_i0 = !has_gu ? 0 : (gu_shared ? w * plan.pp : ((w - sh_wgs) % (I / plan.pp)) * plan.pp);
+    const bool gu_shared = w >= plan.n_rt;
+    const int gu_group = gu_shared ? k : (int)(((uint64_t)(u32)w * plan.magic_wpg) >> 32);
+    const int gu_i0 = (gu_shared ? w - plan.n_rt : w - gu_group * (I / plan.pp)) * plan.pp;
     const int Igu = gu_shared ? Ish : I;
 
+    // slot s of a wave holds gate/up row task t (t < pp: gate row, else up
+    // row); a slot past 2*pp re-loads task 0
     Unit<FMT> gu_un[MG][QG];
     int gu_task[MG];
 #pragma unroll
-    for (int s = 0; s < MG; ++s) gu_task[s] = -1;
+    for (int s = 0; s < MG; ++s) {
+        const int t = (wv + 4 * s) * RPWg + rsg;
+        gu_task[s] = t < 2 * plan.pp ? t : -1;
+    }
     auto issue_gu = [&](const uint8_t *c13, const uint8_t *s13) {
 #pragma unroll
         for (int s = 0; s < MG; ++s) {
-            const int t = (wv + 4 * s) * RPWg + rsg;          // t < pp: gate row, else up row
-            gu_task[s] = (has_gu && t < 2 * plan.pp) ? t : -1;
-            if (gu_task[s] >= 0) {
-                const int row = (t < plan.pp) ? gu_i0 + t : Igu + gu_i0 + (t - plan.pp);
-                const uint8_t *c = c13 + (int64_t)row * crbH;
-                const uint8_t *sc = s13 + (int64_t)row * srbH;
+            const int t = gu_task[s] >= 0 ? gu_task[s] : 0;
+            const int row = (t < plan.pp) ? gu_i0 + t : Igu + gu_i0 + (t - plan.pp);
+            const uint8_t *c = c13 + (int64_t)row * crbH;
+            const uint8_t *sc = s13 + (int64_t)row * srbH;
 #pragma unroll
-                for (int q = 0; q < QG; ++q) {
-                    const int u = lrg + LPRg * q;
-                    if (u < UH) load_unit<FMT>(gu_un[s][q], c, sc, u);
-                }
+            for (int q = 0; q < QG; ++q) {
+                const int u = lrg + LPRg * q;
+                load_unit<FMT>(gu_un[s][q], c, sc, u < UH ? u : lrg);
             }
         }
     };
-    if (gu_shared) issue_gu(ly.sh13c, ly.sh13s);      // before routing: nothing to wait for
 
     // ------------------------------------------------ route (every workgroup, wave 0)
     if (wv == 0) {
@@ -157,52 +185,16 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     }
     __syncthreads();
 
-    // ------------------------------------------------ issue the remaining weight loads
-    // Every expert id needed is read from LDS first, then the gate/up and the
-    // down loads are issued back to back (nothing in between that would make
-    // the compiler wait for the first batch before issuing the second).
-    const int o0 = w * plan.rw;
-    const int nr = max(0, min(H, o0 + plan.rw) - o0);
-    const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
-    const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
-    int dn_g[MD], dn_r[MD], dn_e[MD];
+    // ------------------------------------------------ the remaining weight loads, gate | up dots
+    // (one issue site for every workgroup: loads issued on two different paths
+    // into the same registers make the compiler wait for all of them)
+    const int gu_e = gu_shared ? 0 : S.sel[gu_group];
+    issue_gu(gu_shared ? ly.sh13c : ly.w13c + (int64_t)gu_e * 2 * I * crbH,
+             gu_shared ? ly.sh13s : ly.w13s + (int64_t)gu_e * 2 * I * srbH);
+    auto gu_dots = [&]() {
 #pragma unroll
-    for (int s = 0; s < MD; ++s) {
-        // down task d in [0, NG*nr): group d / rw, local row d % rw
-        const int d = (wv + 4 * s) * RPWd + rsd;
-        const int g = (int)__umulhi((u32)d, plan.magic_rw);
-        const int r = d - g * plan.rw;
-        const bool ok = (nr > 0) && (g < NG) && (r < nr);
-        dn_g[s] = ok ? g : -1;
-        dn_r[s] = r;
-        dn_e[s] = ok ? S.sel[g] : 0;
-    }
-    const int gu_e = (has_gu && !gu_shared) ? S.sel[gu_group] : 0;
-    if (has_gu && !gu_shared) issue_gu(ly.w13c + (int64_t)gu_e * 2 * I * crbH, ly.w13s + (int64_t)gu_e * 2 * I * srbH);
-    Unit<FMT> dn_un[MD][QD];
-#pragma unroll
-    for (int s = 0; s < MD; ++s) {
-        if (dn_g[s] >= 0) {
-            const int e = dn_e[s], r = dn_r[s];
-            const int Ig = (e >= 0) ? I : Ish;
-            const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
-            const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o0 + r) * crbI : ly.sh2c + (int64_t)(o0 + r) * crbI;
-            const uint8_t *sc = (e >= 0) ? ly.w2s + ((int64_t)e * H + o0 + r) * srbI : ly.sh2s + (int64_t)(o0 + r) * srbI;
-            const int Ug = Ig / 32;
-#pragma unroll
-            for (int q = 0; q < QD; ++q) {
-                const int u = lrd + LPRd * q;
-                if (u < Ug) load_unit<FMT>(dn_un[s][q], c, sc, u);
-            }
-        }
-    }
-
-    // ------------------------------------------------ gate | up dots, h published with the call tag
-    const u32 tag = S.tag;
-#pragma unroll
-    for (int s = 0; s < MG; ++s) {
-        float acc = 0.f;
-        if (gu_task[s] >= 0) {
+        for (int s = 0; s < MG; ++s) {
+            float acc = 0.f;
 #pragma unroll
             for (int q = 0; q < QG; ++q) {
                 const int u = lrg + LPRg * q;
@@ -214,106 +206,145 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
                     acc = unit_dot<FMT>(wd, xr[q][0], s0, s1, acc);
                 }
             }
+            acc = group_sum_dpp(acc, LPRg);
+            if (gu_task[s] >= 0 && lrg == 0) S.gu[gu_task[s]] = acc;
         }
-        acc = group_sum_dpp(acc, LPRg);
-        if (gu_task[s] >= 0 && lrg == 0) S.gu[gu_task[s]] = acc;
-    }
-    __syncthreads();
-    if (has_gu && tid < plan.pp) {
-        const float h = silu_f32(S.gu[tid]) * S.gu[plan.pp + tid];
-        d1_st64_relaxed(hw + (size_t)gu_group * Imax + gu_i0 + tid,
-                        ((uint64_t)tag << 32) | __builtin_bit_cast(u32, h));
-    }
+    };
+    const int o0 = w * plan.rw;
+    const int nr = max(0, min(H, o0 + plan.rw) - o0);
 
-    // ------------------------------------------------ gather all of h (poll until every tag is current)
-    // into LDS as bf16 hi/lo words: per group, unit u = 16 words of hi pairs then 16 words of lo pairs.
-    // Batches of NB 16-byte pieces (2 elements each) per thread, every batch loaded at once (each
-    // batch costs a device-coherent round trip, so a batch covers a whole layer of the common sizes).
-    {
-        constexpr int NB = 12;   // 3,072 pieces per batch: one round trip for 11 groups of 512
-        const int total2 = NG * Imax / 2;
-        const __amdgpu_buffer_rsrc_t hr =
-            __builtin_amdgcn_make_buffer_rsrc(hw, (short)0, (int)(NG * Imax * 8), 0x00020000);
-        typedef __attribute__((ext_vector_type(4))) u32 v4u;
-        u32 spins = 0;
-        for (int base = 0; base < total2; base += 256 * NB) {
-            // pieces of this batch: piece j holds elements e0, e0 + 1 of group g (e0 < Ig: needed)
-            u32 val[NB][2];
-            bool need[NB];
+    if (wv < 3) {
+        // ---------------------------------------------- waves 0..2: down rows in flight, gate/up dots
+        // (separate code from wave 3's, so that the compiler's count of
+        // outstanding loads is exact on both sides)
+        const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
+        const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
+        int dn_g[MD], dn_r[MD];
+        Unit<FMT> dn_un[MD][QD];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int q = base + tid + 256 * j;
-                need[j] = false;
-                if (q < total2) {
-                    const int g = (2 * q) / Imax, e0 = (2 * q) % Imax;
-                    need[j] = e0 < ((S.sel[g] >= 0) ? I : Ish);
-                }
-                val[j][0] = val[j][1] = 0u;
-            }
-            // poll: reload every needed piece until both of its tags are current
-            for (;;) {
-                bool all = true;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const u32 off = (u32)(base + tid + 256 * j) * 16u;
-                    const v4u p = need[j] ? __builtin_amdgcn_raw_buffer_load_b128(hr, (int)off, 0, 16)   // sc1
-                                          : v4u{0u, tag, 0u, tag};
-                    val[j][0] = p.x;
-                    val[j][1] = p.z;
-                    all = all && (p.y == tag) && (p.w == tag);
-                }
-                if (all) break;
-                if (spins++ >= a.spin_limit) { d1_st_relaxed(&hdr[WS_ERR], 1u); break; }
-                __builtin_amdgcn_s_sleep(1);
-            }
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int q = base + tid + 256 * j;
-                if (q < total2) {
-                    const int g = (2 * q) / Imax, e0 = (2 * q) % Imax;   // elements e0, e0+1 of group g
-                    const float h0 = __builtin_bit_cast(float, val[j][0]), h1 = __builtin_bit_cast(float, val[j][1]);
-                    const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
-                    const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
-                    const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-                    const int pe = e0 >> 1;
-                    u32 *dst = s_h + g * Imax + 32 * (pe >> 4);
-                    dst[pe & 15] = hi0 | (hi1 << 16);
-                    dst[16 + (pe & 15)] = lo0 | (lo1 << 16);
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // ------------------------------------------------ down dots, then the combine
-#pragma unroll
-    for (int s = 0; s < MD; ++s) {
-        float acc = 0.f;
-        if (dn_g[s] >= 0) {
-            const int g = dn_g[s];
-            const int Ug = ((S.sel[g] >= 0) ? I : Ish) / 32;
+        for (int s = 0; s < MD; ++s) {
+            // down task d in [0, NG*nr): group d / rw, local row d % rw; idle
+            // slots re-load task 0 (group 0, first row)
+            const int d = (wv + 3 * s) * RPWd + rsd;
+            const int g = (int)(((uint64_t)(u32)d * plan.magic_rw) >> 32);
+            const int r = d - g * plan.rw;
+            const bool ok = (nr > 0) && (g < NG) && (r < nr);
+            dn_g[s] = ok ? g : -1;
+            dn_r[s] = ok ? r : 0;
+            const int e = S.sel[ok ? g : 0], o = min(o0 + dn_r[s], H - 1);
+            const int Ig = (e >= 0) ? I : Ish;
+            const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
+            const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o) * crbI : ly.sh2c + (int64_t)o * crbI;
+            const uint8_t *sc = (e >= 0) ? ly.w2s + ((int64_t)e * H + o) * srbI : ly.sh2s + (int64_t)o * srbI;
+            const int Ug = Ig / 32;
 #pragma unroll
             for (int q = 0; q < QD; ++q) {
                 const int u = lrd + LPRd * q;
-                if (u < Ug) {
-                    const uint4 *hp = reinterpret_cast<const uint4 *>(s_h + g * Imax + 32 * u);
-                    u32 xh[16], xl[16];
-#pragma unroll
-                    for (int vv = 0; vv < 4; ++vv) {
-                        const uint4 A = hp[vv], B = hp[4 + vv];
-                        xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
-                        xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
-                    }
-                    u32 wd[16];
-                    decode_unit<FMT, DEC>(dn_un[s][q], Lt, wd);
-                    float s0, s1;
-                    unit_scales<FMT>(dn_un[s][q], Lt, s0, s1);
-                    acc = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc);
-                }
+                load_unit<FMT>(dn_un[s][q], c, sc, u < Ug ? u : lrd);
             }
         }
-        acc = group_sum_dpp(acc, LPRd);
-        if (dn_g[s] >= 0 && lrd == 0) S.y[dn_g[s] * D1_MAX_RW + dn_r[s]] = acc;
+        gu_dots();
+        ring_barrier();   // gate/up results in LDS (bare: the down rows may still be in flight)
+        ring_barrier();   // all of h in LDS
+
+        // ---------------------------------------------- down dots
+#pragma unroll
+        for (int s = 0; s < MD; ++s) {
+            float acc = 0.f;
+            if (dn_g[s] >= 0) {
+                const int g = dn_g[s];
+                const int Ug = ((g < k) ? I : Ish) / 32;
+#pragma unroll
+                for (int q = 0; q < QD; ++q) {
+                    const int u = lrd + LPRd * q;
+                    if (u < Ug) {
+                        const uint4 *hb = reinterpret_cast<const uint4 *>(s_h + g * Imax + 32 * u);
+                        const int sw = d1_piece_swz(u);
+                        u32 xh[16], xl[16];
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv) {
+                            const uint4 A = hb[vv ^ sw], B = hb[(4 + vv) ^ sw];
+                            xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
+                            xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
+                        }
+                        u32 wd[16];
+                        decode_unit<FMT, DEC>(dn_un[s][q], Lt, wd);
+                        float s0, s1;
+                        unit_scales<FMT>(dn_un[s][q], Lt, s0, s1);
+                        acc = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc);
+                    }
+                }
+            }
+            acc = group_sum_dpp(acc, LPRd);
+            if (dn_g[s] >= 0 && lrd == 0) S.y[dn_g[s] * D1_MAX_RW + dn_r[s]] = acc;
+        }
+    } else {
+        // ---------------------------------------------- wave 3: gate/up dots, then the exchange
+        gu_dots();
+        ring_barrier();   // gate/up results in LDS
+        const u32 tag = S.tag;
+        // h of this workgroup's pairs as bf16 hi/lo pair words, in unit layout
+        if (2 * lane < plan.pp) {
+            const int j = 2 * lane;
+            const float h0 = silu_f32(S.gu[j]) * S.gu[plan.pp + j];
+            const float h1 = silu_f32(S.gu[j + 1]) * S.gu[plan.pp + j + 1];
+            const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
+            const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
+            const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
+            const int e0 = gu_i0 + j;
+            u32 *dst = hp + (size_t)gu_group * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
+            d1_st_relaxed(dst, hi0 | (hi1 << 16));
+            d1_st_relaxed(dst + 16, lo0 | (lo1 << 16));
+        }
+        wait_vm<0>();   // this wave has nothing else in flight: only the h stores are waited for
+        if (lane == 0) d1_st_relaxed(&flags[w], tag);
+
+        // poll every workgroup's flag; copy each expert group's h into LDS as
+        // soon as all of its producers are ready
+        typedef __attribute__((ext_vector_type(4))) u32 v4u;
+        const int G = plan.g_gu;
+        const __amdgpu_buffer_rsrc_t fr = rsrc_of(flags, (uint64_t)G * 4);
+        const __amdgpu_buffer_rsrc_t hr = rsrc_of(hp, (uint64_t)NG * Imax * 4);
+        uint64_t pending = (NG >= 64) ? ~0ull : ((1ull << NG) - 1ull);
+        u32 spins = 0;
+        for (;;) {
+            uint64_t notready = 0;
+            for (int c = 0; c < G; c += 256) {
+                const int w0 = c + 4 * lane;
+                const v4u f = __builtin_amdgcn_raw_buffer_load_b128(fr, w0 * 4, 0, 16);   // sc1
+                const u32 fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int wi = w0 + i;
+                    if (wi < G && fv[i] != tag) {
+                        const int g = wi < plan.n_rt ? (int)(((uint64_t)(u32)wi * plan.magic_wpg) >> 32) : k;
+                        notready |= 1ull << g;
+                    }
+                }
+            }
+            notready = (uint64_t)wave_or_u32((u32)notready) | ((uint64_t)wave_or_u32((u32)(notready >> 32)) << 32);
+            const uint64_t ready = pending & ~notready;
+            for (uint64_t m = ready; m != 0; m &= m - 1) {
+                const int g = __builtin_ctzll(m);
+                const int npc = ((g < k) ? I : Ish) / 4;   // 16-byte pieces of the group's h
+                for (int p0 = 0; p0 < npc; p0 += 64) {
+                    const int p = p0 + lane;
+                    if (p < npc) {
+                        // LDS piece p = (unit p/8, slot p%8) takes piece slot ^ swz(unit) of that unit
+                        const int u = p >> 3, src = (u << 3) | ((p & 7) ^ d1_piece_swz(u));
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (lds_void_t *)(s_h + g * Imax + 4 * p0), 16,
+                                                                 (u32)((g * Imax) * 4 + src * 16), 0, 0, 16);
+                    }
+                }
+            }
+            pending &= ~ready;
+            if (pending == 0 && a.spin_limit != 0u) break;
+            // bounded; spin_limit 0 (the test hook) expires at once
+            if (spins++ >= a.spin_limit) { d1_st_relaxed(&hdr[WS_ERR], 1u); break; }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        wait_vm<0>();
+        ring_barrier();   // all of h in LDS
     }
     __syncthreads();
     for (int r = tid; r < nr; r += 256) {
@@ -325,7 +356,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     }
     // every workgroup leaves its tag as the call counter (a max, so the counter
     // never moves back even after an expired wait)
-    if (tid == 0) __hip_atomic_fetch_max(&hdr[WS_EPOCH], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_fetch_max(&hdr[WS_EPOCH], S.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace moeq
@@ -364,14 +395,20 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
         if (L.I % pp || (L.Ish > 0 && L.Ish % pp)) break;
         if (2 * pp > 4 * MG * RPWg) break;
         const int g_gu = (L.k * L.I + L.Ish) / pp;
-        if (g_gu > cap) continue;
-        int G = g_gu > 0 ? g_gu : 1;
+        if (g_gu > cap || g_gu > D1_MAX_WGS) continue;
+        const int G = g_gu;
         const int rw = (L.H + G - 1) / G;
         if (rw > D1_MAX_RW) continue;
-        if (NG * rw > 4 * MD * RPWd) continue;
-        // every workgroup must publish h (see the tag argument above): no down-only workgroups
-        if ((L.H + rw - 1) / rw > g_gu) continue;
-        D1Plan plan{pp, g_gu, rw, (u32)(0xFFFFFFFFull / (u32)rw + 1u), down_lanes_per_row(L.I, L.Ish)};
+        if (NG * rw > 3 * MD * RPWd) continue;   // down tasks live on waves 0..2
+        const int wpg = L.I / pp;
+        // floor(2^32 / d) + 1: exact quotients for the small numerators used (checked below)
+        D1Plan plan{pp, g_gu, L.k * wpg, (1ull << 32) / (uint64_t)wpg + 1u, rw, (1ull << 32) / (uint64_t)rw + 1u,
+                    down_lanes_per_row(L.I, L.Ish)};
+        // the reciprocal multiplies are exact over the ranges the kernel uses
+        for (int v = 0; v < G; ++v)
+            if ((int)(((uint64_t)v * plan.magic_wpg) >> 32) != v / wpg) return hipErrorNotSupported;
+        for (int v = 0; v < 3 * MD * RPWd + 4 * RPWd; ++v)
+            if ((int)(((uint64_t)v * plan.magic_rw) >> 32) != v / rw) return hipErrorNotSupported;
         hipLaunchKernelGGL(kern, dim3(G), dim3(256), dyn, s, a, plan);
         return hipGetLastError();
     }
@@ -382,7 +419,7 @@ template <int FMT, int DEC, int QG, int QD>
 static hipError_t decode1_q(const DecodeArgs &a, hipStream_t s) {
     hipError_t e = decode1_try<FMT, DEC, QG, QD, 2, 4>(a, s);
     if (e != hipErrorNotSupported) return e;
-    e = decode1_try<FMT, DEC, QG, QD, 8, 8>(a, s);
+    e = decode1_try<FMT, DEC, QG, QD, 8, 6>(a, s);
     if (e != hipErrorNotSupported) return e;
     return decode1_try<FMT, DEC, QG, QD, 16, 12>(a, s);
 }

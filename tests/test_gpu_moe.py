@@ -172,3 +172,25 @@ def test_bounded_wait_expiry_is_reported_then_recovers():
     _, _, ref = oracle_layer(cfg, x, l)
     assert max_rel_err(out, ref) <= PARITY_TOL
     assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
+
+
+def test_single_token_wait_expiry_is_reported_then_recovers():
+    """The one-token kernel's bounded wait (its exchange of h between
+    workgroups), forced to expire by the test hook: the status call reports
+    it once, and the following calls on the same workspace match the oracle."""
+    require_gpu()
+    cfg = SMALL
+    L = _layer(cfg)
+    x, l = _inputs(cfg, 1, sub=7)
+    xd, ld = dev_bf16(x), torch.from_numpy(l).cuda()
+    ws = moeq.workspace(L, 1)
+    moeq.moe_layer_decode(L, xd, ld, flags=F32 | moeq.MOE_DEBUG_SPIN_LIMIT, ws=ws)
+    with pytest.raises(moeq.MoeError) as ei:
+        moeq.moe_workspace_status(ws)
+    assert ei.value.code == moeq.MOE_EKERNEL
+    assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
+    _, _, ref = oracle_layer(cfg, x, l)
+    for _ in range(3):
+        out = moeq.moe_layer_decode(L, xd, ld, flags=F32, ws=ws).cpu().numpy()
+        assert max_rel_err(out, ref) <= PARITY_TOL
+        assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
