@@ -3,10 +3,13 @@
 // docs/INTEL.md, "The engine itself on Intel": router_top10, shared_expert).
 //
 // With one token every selected expert serves exactly one row, so the work is
-// static once the token is routed:
-//   gate | up : workgroup w computes PP consecutive (gate row, up row) pairs
-//               of ONE expert; the routed experts' workgroups come first and
-//               the shared expert's last;
+// static once the token is routed.  One workgroup of 16 waves per CU (a burst
+// of loads streams at the rate of the waves issuing it, so every CU needs
+// many waves, not many loads per wave):
+//   gate | up : the layer's P = k*I + Ish (gate row, up row) pairs, routed
+//               experts in rank order then the shared expert, are split into
+//               G equal ranges with even bounds; workgroup w computes range w
+//               (it may straddle two experts);
 //   down      : workgroup w computes RW consecutive output rows for EVERY
 //               selected expert and combines them itself, in rank order, so no
 //               partial sums leave the CU.
@@ -17,19 +20,21 @@
 // the compiler counts outstanding loads exactly and the gate/up dots wait for
 // the gate/up rows only, not for the down rows behind them.
 //
-// The down rows need every expert's h.  Wave 3 of each workgroup is its
-// exchange wave (it loads no down rows of its own): it stores the
-// workgroup's h as bf16 hi/lo pairs with device-coherent stores, waits for
-// them, then sets the workgroup's ready flag to the call tag.  It then polls
-// all flags (one 4-byte word per workgroup, so a poll costs little) and, as
-// soon as every producer of an expert group is ready, copies that group's h
-// straight from memory into LDS (buffer-load-to-LDS, no registers), until all
-// groups are in.  The tag is the workspace's call counter + 1: every
-// workgroup reads the counter on entry and raises it to counter + 1 on exit.
-// That is safe because every workgroup publishes h and none leaves before all
-// h is published, so none can finish before all have read the counter; and it
-// stays correct when the launch is replayed from a captured graph.
+// The down rows need every expert's h.  The last wave of each workgroup is its
+// exchange wave (it loads no down rows): it stores the workgroup's h as bf16
+// hi/lo pairs with device-coherent stores, waits for them, then sets the
+// workgroup's ready flag to the call tag.  It then polls all flags (one 4-byte
+// word per workgroup) and, as soon as every producer of an expert group is
+// ready, copies that group's h straight from memory into LDS
+// (buffer-load-to-LDS), until all groups are in.  The tag is the workspace's
+// call counter + 1: every workgroup reads the counter on entry and raises it
+// to counter + 1 on exit.  That is safe because every workgroup publishes h
+// and none leaves before all h is published, so none can finish before all
+// have read the counter; and it stays correct when the launch is replayed
+// from a captured graph.
 #pragma once
+
+#include <algorithm>
 
 #include "kernels.h"
 #include "rowdot.h"
@@ -50,15 +55,22 @@ __device__ inline u32 wave_or_u32(u32 v) {
            (u32)__builtin_amdgcn_readlane((int)v, 32) | (u32)__builtin_amdgcn_readlane((int)v, 48);
 }
 
+constexpr int D1_NW = 16;                  // waves per workgroup
+constexpr int D1_THREADS = 64 * D1_NW;
+constexpr int D1_XW = D1_NW - 1;           // the exchange wave
+constexpr int D1_MAX_PAIRS_WG = 128;       // gate/up pairs per workgroup (two per lane of the exchange wave)
+
 struct D1Plan {
-    int pp;            // gate/up pairs per workgroup (divides I and the shared I)
-    int g_gu;          // workgroups; every one has gate/up work
-    int n_rt;          // workgroups of the routed experts (the first ones)
-    uint64_t magic_wpg;   // w / (I / pp) == (w * magic_wpg) >> 32 for w < g_gu
-    int rw;            // output rows per workgroup
-    uint64_t magic_rw;    // d / rw == (d * magic_rw) >> 32 for the small d used here
-    int lpr_d;         // lanes per row of the down projection (down_lanes_per_row)
+    int G;              // workgroups
+    int P;              // gate/up pairs of the layer
+    int rw;             // output rows per workgroup
+    uint64_t magic_rw;  // d / rw == (d * magic_rw) >> 32 for the small d used here
+    int lpr_d;          // lanes per row of the down projection (down_lanes_per_row)
 };
+
+// First pair of workgroup w (even, so the two elements of an h word never
+// belong to different workgroups)
+__host__ __device__ inline int d1_pair_lo(int P, int G, int w) { return 2 * (int)(((int64_t)(P / 2) * w) / G); }
 
 constexpr int D1_MAX_GROUPS = 33;           // k <= 32 routed + shared
 constexpr int D1_H_LDS_WORDS = 16384;       // all of h as bf16 hi/lo words (64 KiB)
@@ -68,7 +80,7 @@ struct D1Shared {
     int sel[D1_MAX_GROUPS];         // expert of group g (-1: shared)
     float wsel[D1_MAX_GROUPS];      // its gate weight (1 for the shared expert)
     u32 tag;
-    float gu[2 * 64];               // gate/up dot results of this workgroup (pp <= 64)
+    float gu[2 * D1_MAX_PAIRS_WG];  // gate/up dot results of this workgroup
     float y[D1_MAX_GROUPS * D1_MAX_RW];   // down results: [group][local row]
 };
 
@@ -89,7 +101,7 @@ __host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
 __device__ inline int d1_piece_swz(int u) { return (u >> 1) & 7; }
 
 template <int FMT, int DEC, int QG, int QD, int MG, int MD>
-__global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan) {
+__global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Plan plan) {
     constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
     __shared__ u32 s_pair[PAIR];
     __shared__ float s_scale[LUT_SCALE];
@@ -118,10 +130,10 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
         else route_load_logits<16>(a.logits, E, lane, lgt);
     }
     // the routing wave does nothing else until it has routed: the call tag and
-    // the tables come from the other three waves (first used after the
-    // barrier that follows routing)
+    // the tables come from the other waves (first used after the barrier that
+    // follows routing)
     if (tid == 64) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
-    if (wv > 0) build_luts<FMT>(Lt, tid - 64, 192, DEC == DEC_LUT);
+    if (wv > 0) build_luts<FMT>(Lt, tid - 64, D1_THREADS - 64, DEC == DEC_LUT);
     const int UH = H / 32, LPRg = lanes_per_row(UH), RPWg = WAVE / LPRg;
     const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
     u32 xr[QG][1][16];
@@ -129,37 +141,6 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
         const uint16_t *xp[1] = {a.x};
         load_x_units<QG, 1>(xr, xp, UH, lrg, LPRg);
     }
-
-    // ------------------------------------------------ gate/up share: group, first pair
-    const int w = blockIdx.x;
-    const bool gu_shared = w >= plan.n_rt;
-    const int gu_group = gu_shared ? k : (int)(((uint64_t)(u32)w * plan.magic_wpg) >> 32);
-    const int gu_i0 = (gu_shared ? w - plan.n_rt : w - gu_group * (I / plan.pp)) * plan.pp;
-    const int Igu = gu_shared ? Ish : I;
-
-    // slot s of a wave holds gate/up row task t (t < pp: gate row, else up
-    // row); a slot past 2*pp re-loads task 0
-    Unit<FMT> gu_un[MG][QG];
-    int gu_task[MG];
-#pragma unroll
-    for (int s = 0; s < MG; ++s) {
-        const int t = (wv + 4 * s) * RPWg + rsg;
-        gu_task[s] = t < 2 * plan.pp ? t : -1;
-    }
-    auto issue_gu = [&](const uint8_t *c13, const uint8_t *s13) {
-#pragma unroll
-        for (int s = 0; s < MG; ++s) {
-            const int t = gu_task[s] >= 0 ? gu_task[s] : 0;
-            const int row = (t < plan.pp) ? gu_i0 + t : Igu + gu_i0 + (t - plan.pp);
-            const uint8_t *c = c13 + (int64_t)row * crbH;
-            const uint8_t *sc = s13 + (int64_t)row * srbH;
-#pragma unroll
-            for (int q = 0; q < QG; ++q) {
-                const int u = lrg + LPRg * q;
-                load_unit<FMT>(gu_un[s][q], c, sc, u < UH ? u : lrg);
-            }
-        }
-    };
 
     // ------------------------------------------------ route (every workgroup, wave 0)
     if (wv == 0) {
@@ -185,12 +166,32 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     }
     __syncthreads();
 
-    // ------------------------------------------------ the remaining weight loads, gate | up dots
-    // (one issue site for every workgroup: loads issued on two different paths
-    // into the same registers make the compiler wait for all of them)
-    const int gu_e = gu_shared ? 0 : S.sel[gu_group];
-    issue_gu(gu_shared ? ly.sh13c : ly.w13c + (int64_t)gu_e * 2 * I * crbH,
-             gu_shared ? ly.sh13s : ly.w13s + (int64_t)gu_e * 2 * I * srbH);
+    // ------------------------------------------------ gate/up rows of this workgroup's pairs
+    // row task t < 2n: t < n is the gate row of pair pl + t, else the up row of pair pl + t - n;
+    // pair p belongs to group min(p / I, k) (routed experts in rank order, then the shared one)
+    const int w = blockIdx.x, kI = k * I;
+    const int pl = d1_pair_lo(plan.P, plan.G, w), n = d1_pair_lo(plan.P, plan.G, w + 1) - pl;
+    Unit<FMT> gu_un[MG][QG];
+    int gu_task[MG];
+#pragma unroll
+    for (int s = 0; s < MG; ++s) {
+        const int t = (wv + D1_NW * s) * RPWg + rsg;
+        gu_task[s] = t < 2 * n ? t : -1;
+        const int tc = t < 2 * n ? t : 0;   // idle slots re-load task 0
+        const int p = pl + (tc < n ? tc : tc - n);
+        const int g = min(p / I, k);
+        const int i = p - g * I;
+        const int e = g < k ? S.sel[g] : -1;
+        const int Ig = g < k ? I : Ish;
+        const int row = tc < n ? i : Ig + i;
+        const uint8_t *c = (e >= 0 ? ly.w13c + (int64_t)e * 2 * I * crbH : ly.sh13c) + (int64_t)row * crbH;
+        const uint8_t *sc = (e >= 0 ? ly.w13s + (int64_t)e * 2 * I * srbH : ly.sh13s) + (int64_t)row * srbH;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            const int u = lrg + LPRg * q;
+            load_unit<FMT>(gu_un[s][q], c, sc, u < UH ? u : lrg);
+        }
+    }
     auto gu_dots = [&]() {
 #pragma unroll
         for (int s = 0; s < MG; ++s) {
@@ -213,10 +214,10 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
     const int o0 = w * plan.rw;
     const int nr = max(0, min(H, o0 + plan.rw) - o0);
 
-    if (wv < 3) {
-        // ---------------------------------------------- waves 0..2: down rows in flight, gate/up dots
-        // (separate code from wave 3's, so that the compiler's count of
-        // outstanding loads is exact on both sides)
+    if (wv < D1_XW) {
+        // ---------------------------------------------- worker waves: down rows in flight, gate/up dots
+        // (separate code from the exchange wave's, so that the compiler's count
+        // of outstanding loads is exact on both sides)
         const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
         const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
         int dn_g[MD], dn_r[MD];
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
         for (int s = 0; s < MD; ++s) {
             // down task d in [0, NG*nr): group d / rw, local row d % rw; idle
             // slots re-load task 0 (group 0, first row)
-            const int d = (wv + 3 * s) * RPWd + rsd;
+            const int d = (wv + D1_XW * s) * RPWd + rsd;
             const int g = (int)(((uint64_t)(u32)d * plan.magic_rw) >> 32);
             const int r = d - g * plan.rw;
             const bool ok = (nr > 0) && (g < NG) && (r < nr);
@@ -279,20 +280,20 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
             if (dn_g[s] >= 0 && lrd == 0) S.y[dn_g[s] * D1_MAX_RW + dn_r[s]] = acc;
         }
     } else {
-        // ---------------------------------------------- wave 3: gate/up dots, then the exchange
+        // ---------------------------------------------- exchange wave: gate/up dots, then the exchange
         gu_dots();
         ring_barrier();   // gate/up results in LDS
         const u32 tag = S.tag;
         // h of this workgroup's pairs as bf16 hi/lo pair words, in unit layout
-        if (2 * lane < plan.pp) {
+        if (2 * lane < n) {
             const int j = 2 * lane;
-            const float h0 = silu_f32(S.gu[j]) * S.gu[plan.pp + j];
-            const float h1 = silu_f32(S.gu[j + 1]) * S.gu[plan.pp + j + 1];
+            const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
+            const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
             const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
             const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
             const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-            const int e0 = gu_i0 + j;
-            u32 *dst = hp + (size_t)gu_group * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
+            const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
+            u32 *dst = hp + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
             d1_st_relaxed(dst, hi0 | (hi1 << 16));
             d1_st_relaxed(dst + 16, lo0 | (lo1 << 16));
         }
@@ -300,9 +301,10 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
         if (lane == 0) d1_st_relaxed(&flags[w], tag);
 
         // poll every workgroup's flag; copy each expert group's h into LDS as
-        // soon as all of its producers are ready
+        // soon as all of its producers are ready.  A workgroup's pairs span
+        // groups min(lo / I, k) .. min((hi - 1) / I, k).
         typedef __attribute__((ext_vector_type(4))) u32 v4u;
-        const int G = plan.g_gu;
+        const int G = plan.G;
         const __amdgpu_buffer_rsrc_t fr = rsrc_of(flags, (uint64_t)G * 4);
         const __amdgpu_buffer_rsrc_t hr = rsrc_of(hp, (uint64_t)NG * Imax * 4);
         uint64_t pending = (NG >= 64) ? ~0ull : ((1ull << NG) - 1ull);
@@ -317,8 +319,9 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
                 for (int i = 0; i < 4; ++i) {
                     const int wi = w0 + i;
                     if (wi < G && fv[i] != tag) {
-                        const int g = wi < plan.n_rt ? (int)(((uint64_t)(u32)wi * plan.magic_wpg) >> 32) : k;
-                        notready |= 1ull << g;
+                        const int lo = d1_pair_lo(plan.P, G, wi), hi = d1_pair_lo(plan.P, G, wi + 1);
+                        const int g0 = min(lo / I, k), g1 = min((hi - 1) / I, k);
+                        notready |= ((2ull << g1) - 1ull) & ~((1ull << g0) - 1ull);
                     }
                 }
             }
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
         ring_barrier();   // all of h in LDS
     }
     __syncthreads();
-    for (int r = tid; r < nr; r += 256) {
+    for (int r = tid; r < nr; r += D1_THREADS) {
         float acc = 0.f;
         for (int g = 0; g < k; ++g) acc = __builtin_fmaf(S.wsel[g], S.y[g * D1_MAX_RW + r], acc);
         if (Ish > 0) acc += S.y[k * D1_MAX_RW + r];
@@ -364,16 +367,17 @@ __global__ __launch_bounds__(256) void decode1_kernel(DecodeArgs a, D1Plan plan)
 namespace moeq {
 
 template <typename K>
-static int d1_coresident(K kernel, size_t dyn_lds) {
-    int dev = 0, cus = 0;
+static int d1_coresident(K kernel, size_t dyn_lds, int &cus) {
+    int dev = 0;
+    cus = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (cus <= 0) cus = 1;
     int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void *>(kernel), 256, dyn_lds) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void *>(kernel), D1_THREADS,
+                                                     dyn_lds) != hipSuccess ||
         per <= 0)
-        per = 1;
+        per = 0;
     return per * cus;
 }
 
@@ -386,42 +390,38 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
     const int NG = L.k + (L.Ish > 0 ? 1 : 0);
     const int Imax = L.I > L.Ish ? L.I : L.Ish;
     const size_t dyn = (size_t)NG * Imax * 4;
-    const int cap = d1_coresident(kern, dyn);
+    int cus = 0;
+    const int cap = d1_coresident(kern, dyn, cus);
     const int RPWg = WAVE / lanes_per_row(L.H / 32);
     const int RPWd = WAVE / down_lanes_per_row(L.I, L.Ish);
-    // pairs per workgroup: a power of two dividing I and the shared I, at most 64
-    // and what the gate/up slots hold; the smallest that fits the grid
-    for (int pp = 16; pp <= 64; pp *= 2) {
-        if (L.I % pp || (L.Ish > 0 && L.Ish % pp)) break;
-        if (2 * pp > 4 * MG * RPWg) break;
-        const int g_gu = (L.k * L.I + L.Ish) / pp;
-        if (g_gu > cap || g_gu > D1_MAX_WGS) continue;
-        const int G = g_gu;
-        const int rw = (L.H + G - 1) / G;
-        if (rw > D1_MAX_RW) continue;
-        if (NG * rw > 3 * MD * RPWd) continue;   // down tasks live on waves 0..2
-        const int wpg = L.I / pp;
-        // floor(2^32 / d) + 1: exact quotients for the small numerators used (checked below)
-        D1Plan plan{pp, g_gu, L.k * wpg, (1ull << 32) / (uint64_t)wpg + 1u, rw, (1ull << 32) / (uint64_t)rw + 1u,
-                    down_lanes_per_row(L.I, L.Ish)};
-        // the reciprocal multiplies are exact over the ranges the kernel uses
-        for (int v = 0; v < G; ++v)
-            if ((int)(((uint64_t)v * plan.magic_wpg) >> 32) != v / wpg) return hipErrorNotSupported;
-        for (int v = 0; v < 3 * MD * RPWd + 4 * RPWd; ++v)
-            if ((int)(((uint64_t)v * plan.magic_rw) >> 32) != v / rw) return hipErrorNotSupported;
-        hipLaunchKernelGGL(kern, dim3(G), dim3(256), dyn, s, a, plan);
-        return hipGetLastError();
-    }
-    return hipErrorNotSupported;
+    const int P = L.k * L.I + L.Ish;
+    // one workgroup per CU (all must be resident: they wait on each other),
+    // fewer for a small layer (at least 16 pairs each)
+    int G = cus;
+    if (G > P / 16) G = P / 16;
+    if (G > cap) G = cap;
+    if (G > D1_MAX_WGS) G = D1_MAX_WGS;
+    if (G < 1) return hipErrorNotSupported;
+    int nmax = 0;   // the largest pair range
+    for (int w = 0; w < G; ++w) nmax = std::max(nmax, d1_pair_lo(P, G, w + 1) - d1_pair_lo(P, G, w));
+    if (nmax > D1_MAX_PAIRS_WG || 2 * nmax > D1_NW * MG * RPWg) return hipErrorNotSupported;
+    const int rw = (L.H + G - 1) / G;
+    if (rw > D1_MAX_RW || NG * rw > D1_XW * MD * RPWd) return hipErrorNotSupported;
+    // floor(2^32 / rw) + 1: exact quotients for the small numerators used (checked)
+    D1Plan plan{G, P, rw, (1ull << 32) / (uint64_t)rw + 1u, down_lanes_per_row(L.I, L.Ish)};
+    for (int v = 0; v < (D1_XW * MD + D1_NW) * RPWd; ++v)
+        if ((int)(((uint64_t)v * plan.magic_rw) >> 32) != v / rw) return hipErrorNotSupported;
+    hipLaunchKernelGGL(kern, dim3(G), dim3(D1_THREADS), dyn, s, a, plan);
+    return hipGetLastError();
 }
 
 template <int FMT, int DEC, int QG, int QD>
 static hipError_t decode1_q(const DecodeArgs &a, hipStream_t s) {
-    hipError_t e = decode1_try<FMT, DEC, QG, QD, 2, 4>(a, s);
+    hipError_t e = decode1_try<FMT, DEC, QG, QD, 1, 1>(a, s);
     if (e != hipErrorNotSupported) return e;
-    e = decode1_try<FMT, DEC, QG, QD, 8, 6>(a, s);
+    e = decode1_try<FMT, DEC, QG, QD, 3, 2>(a, s);
     if (e != hipErrorNotSupported) return e;
-    return decode1_try<FMT, DEC, QG, QD, 16, 12>(a, s);
+    return decode1_try<FMT, DEC, QG, QD, 8, 4>(a, s);
 }
 
 template <int FMT, int DEC>

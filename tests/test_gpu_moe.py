@@ -194,3 +194,35 @@ def test_single_token_wait_expiry_is_reported_then_recovers():
         out = moeq.moe_layer_decode(L, xd, ld, flags=F32, ws=ws).cpu().numpy()
         assert max_rel_err(out, ref) <= PARITY_TOL
         assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
+
+
+ONE_TOKEN_SHAPES = [
+    # e2m3, two activation units per lane (H = 384) and two h units per lane on the down side
+    MoEConfig("one_e2m3", tokens=2, hidden=384, experts=12, top_k=3, inter=256, shared_inter=128, fmt=2),
+    # H = 2080: 65 units per row, the last one on a second unit slot of lane 0
+    MoEConfig("one_h2080", tokens=2, hidden=2080, experts=32, top_k=8, inter=256),
+    # eight experts of eight: one output row per workgroup
+    MoEConfig("one_k8", tokens=2, hidden=256, experts=8, top_k=8, inter=512),
+    # 4,864 pairs over 256 workgroups: pair ranges straddle two experts
+    MoEConfig("one_straddle", tokens=2, hidden=256, experts=16, top_k=9, inter=512, shared_inter=256),
+]
+
+
+@pytest.mark.parametrize("cfg", ONE_TOKEN_SHAPES, ids=lambda c: c.name)
+def test_single_token_kernel_shapes(cfg):
+    """Shapes that take the one-token kernel's less common paths: against the
+    oracle, and bitwise equal to the same token inside a two-token call (the
+    general kernel)."""
+    require_gpu()
+    L = _layer(cfg)
+    x, l = _inputs(cfg, 2, sub=8)
+    xd, ld = dev_bf16(x), torch.from_numpy(l).cuda()
+    ws = moeq.workspace(L, 2)
+    idx = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+    one = moeq.moe_layer_decode(L, xd[:1], ld[:1], idx_out=idx, flags=F32, ws=ws)
+    two = moeq.moe_layer_decode(L, xd, ld, flags=F32, ws=ws)
+    moeq.moe_workspace_status(ws)
+    ridx, _, ref = oracle_layer(cfg, x[:1], l[:1])
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_rel_err(one.cpu().numpy(), ref) <= PARITY_TOL
+    assert torch.equal(one[0], two[0])
