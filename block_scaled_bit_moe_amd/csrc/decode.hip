@@ -30,9 +30,9 @@ size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
     (void)T;
     (void)k;
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
-    // header | h words of the general kernel | its fp32 partials | the single-token kernel's ready flags and h
+    // header | h words of the general kernel | its fp32 partials | tagged h words of the single-token kernel
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint32_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float) +
-           (size_t)D1_MAX_WGS * sizeof(uint32_t) + (size_t)33 * Imax * sizeof(uint32_t);
+           (size_t)33 * Imax * sizeof(uint64_t);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {

@@ -20,18 +20,21 @@
 // the compiler counts outstanding loads exactly and the gate/up dots wait for
 // the gate/up rows only, not for the down rows behind them.
 //
-// The down rows need every expert's h.  The last wave of each workgroup is its
-// exchange wave (it loads no down rows): it stores the workgroup's h as bf16
-// hi/lo pairs with device-coherent stores, waits for them, then sets the
-// workgroup's ready flag to the call tag.  It then polls all flags (one 4-byte
-// word per workgroup) and, as soon as every producer of an expert group is
-// ready, copies that group's h straight from memory into LDS
-// (buffer-load-to-LDS), until all groups are in.  The tag is the workspace's
-// call counter + 1: every workgroup reads the counter on entry and raises it
-// to counter + 1 on exit.  That is safe because every workgroup publishes h
-// and none leaves before all h is published, so none can finish before all
-// have read the counter; and it stays correct when the launch is replayed
-// from a captured graph.
+//
+// The down rows need every expert's h.  One wave of each workgroup publishes
+// the workgroup's h as 64-bit words, each a bf16 hi or lo pair tagged with the
+// call tag in its upper half, with device-coherent stores (no wait: every
+// word carries its own tag, so no ordering between words is needed).  Then
+// all 16 waves fetch every expert group's words, keep the payload of those
+// whose tag is current (into LDS, compact and swizzled) and fetch again the
+// groups that had a stale word, until all are in.  The first fetch uses
+// ordinary loads, so the 32 workgroups of an XCD share one copy through its
+// L2; later fetches bypass the L2.  The tag is the workspace's call counter +
+// 1: every workgroup reads the counter on entry and raises it to counter + 1
+// on exit.  That is safe because every workgroup publishes h and none leaves
+// before all h is published, so none can finish before all have read the
+// counter; and it stays correct when the launch is replayed from a captured
+// graph.
 #pragma once
 
 #include <algorithm>
@@ -57,7 +60,6 @@ __device__ inline u32 wave_or_u32(u32 v) {
 
 constexpr int D1_NW = 16;                  // waves per workgroup
 constexpr int D1_THREADS = 64 * D1_NW;
-constexpr int D1_XW = D1_NW - 1;           // the exchange wave
 constexpr int D1_MAX_PAIRS_WG = 128;       // gate/up pairs per workgroup (two per lane of the exchange wave)
 
 struct D1Plan {
@@ -80,19 +82,17 @@ struct D1Shared {
     int sel[D1_MAX_GROUPS];         // expert of group g (-1: shared)
     float wsel[D1_MAX_GROUPS];      // its gate weight (1 for the shared expert)
     u32 tag;
+    u32 stale[3][2];                // per fetch round (mod 3): groups with a stale word
     float gu[2 * D1_MAX_PAIRS_WG];  // gate/up dot results of this workgroup
     float y[D1_MAX_GROUPS * D1_MAX_RW];   // down results: [group][local row]
 };
 
-// Regions of the workspace for this kernel: the ready flags (one u32 per
-// workgroup), then h as [group][Imax] u32 words in unit layout (unit u of 32
-// elements: 16 words of bf16 hi pairs, then 16 words of lo pairs).
-__host__ __device__ inline size_t d1_flag_offset(int H, int I, int Ish) {
+// Region of the workspace for this kernel: h as [group][Imax] 64-bit words in
+// unit layout (unit u of 32 elements: 16 words of bf16 hi pairs, then 16 words
+// of lo pairs), each word (call tag << 32) | pair.
+__host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * 4 + (size_t)DEC_MAX_PAIRS * H * 4;
-}
-__host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
-    return d1_flag_offset(H, I, Ish) + (size_t)D1_MAX_WGS * 4;
 }
 
 // LDS layout of h: the 8 16-byte pieces of unit u are stored rotated by
@@ -115,8 +115,7 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     const int NG = k + (Ish > 0 ? 1 : 0);
     const int Imax = I > Ish ? I : Ish;
     u32 *hdr = reinterpret_cast<u32 *>(a.ws);
-    u32 *flags = reinterpret_cast<u32 *>(a.ws + d1_flag_offset(H, I, Ish));
-    u32 *hp = reinterpret_cast<u32 *>(a.ws + d1_h_offset(H, I, Ish));
+    uint64_t *hq = reinterpret_cast<uint64_t *>(a.ws + d1_h_offset(H, I, Ish));
     const int64_t crbH = Fmt<FMT>::code_row_bytes(H), srbH = Fmt<FMT>::scale_row_bytes(H);
 
     // call tag, activation units and the routing logits are all fetched at once;
@@ -133,6 +132,7 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     // the tables come from the other waves (first used after the barrier that
     // follows routing)
     if (tid == 64) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
+    if (tid >= 128 && tid < 134) (&S.stale[0][0])[tid - 128] = 0u;
     if (wv > 0) build_luts<FMT>(Lt, tid - 64, D1_THREADS - 64, DEC == DEC_LUT);
     const int UH = H / 32, LPRg = lanes_per_row(UH), RPWg = WAVE / LPRg;
     const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
@@ -214,140 +214,146 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     const int o0 = w * plan.rw;
     const int nr = max(0, min(H, o0 + plan.rw) - o0);
 
-    if (wv < D1_XW) {
-        // ---------------------------------------------- worker waves: down rows in flight, gate/up dots
-        // (separate code from the exchange wave's, so that the compiler's count
-        // of outstanding loads is exact on both sides)
-        const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
-        const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
-        int dn_g[MD], dn_r[MD];
-        Unit<FMT> dn_un[MD][QD];
+    // ---------------------------------------------- down rows in flight (every wave)
+    const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
+    const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
+    int dn_g[MD], dn_r[MD];
+    Unit<FMT> dn_un[MD][QD];
 #pragma unroll
-        for (int s = 0; s < MD; ++s) {
-            // down task d in [0, NG*nr): group d / rw, local row d % rw; idle
-            // slots re-load task 0 (group 0, first row)
-            const int d = (wv + D1_XW * s) * RPWd + rsd;
-            const int g = (int)(((uint64_t)(u32)d * plan.magic_rw) >> 32);
-            const int r = d - g * plan.rw;
-            const bool ok = (nr > 0) && (g < NG) && (r < nr);
-            dn_g[s] = ok ? g : -1;
-            dn_r[s] = ok ? r : 0;
-            const int e = S.sel[ok ? g : 0], o = min(o0 + dn_r[s], H - 1);
-            const int Ig = (e >= 0) ? I : Ish;
-            const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
-            const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o) * crbI : ly.sh2c + (int64_t)o * crbI;
-            const uint8_t *sc = (e >= 0) ? ly.w2s + ((int64_t)e * H + o) * srbI : ly.sh2s + (int64_t)o * srbI;
-            const int Ug = Ig / 32;
+    for (int s = 0; s < MD; ++s) {
+        // down task d in [0, NG*nr): group d / rw, local row d % rw; idle
+        // slots re-load task 0 (group 0, first row)
+        const int d = (wv + D1_NW * s) * RPWd + rsd;
+        const int g = (int)(((uint64_t)(u32)d * plan.magic_rw) >> 32);
+        const int r = d - g * plan.rw;
+        const bool ok = (nr > 0) && (g < NG) && (r < nr);
+        dn_g[s] = ok ? g : -1;
+        dn_r[s] = ok ? r : 0;
+        const int e = S.sel[ok ? g : 0], o = min(o0 + dn_r[s], H - 1);
+        const int Ig = (e >= 0) ? I : Ish;
+        const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
+        const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o) * crbI : ly.sh2c + (int64_t)o * crbI;
+        const uint8_t *sc = (e >= 0) ? ly.w2s + ((int64_t)e * H + o) * srbI : ly.sh2s + (int64_t)o * srbI;
+        const int Ug = Ig / 32;
+#pragma unroll
+        for (int q = 0; q < QD; ++q) {
+            const int u = lrd + LPRd * q;
+            load_unit<FMT>(dn_un[s][q], c, sc, u < Ug ? u : lrd);
+        }
+    }
+
+    // ---------------------------------------------- gate | up dots, h published
+    gu_dots();
+    ring_barrier();   // gate/up results in LDS (bare: the down rows may still be in flight)
+    const u32 tag = S.tag;
+    if (wv == D1_NW - 1 && 2 * lane < n) {
+        const int j = 2 * lane;
+        const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
+        const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
+        const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
+        const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
+        const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
+        const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
+        uint64_t *dst = hq + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
+        __hip_atomic_store(dst, ((uint64_t)tag << 32) | (hi0 | (hi1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 16, ((uint64_t)tag << 32) | (lo0 | (lo1 << 16)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---------------------------------------------- gather all of h (every wave)
+    // Group g's words are Ig/2 16-byte pieces (two words each: compact words
+    // 2m, 2m+1 of its unit layout).  Pending groups are dealt to quarters of
+    // the workgroup in turn (256 threads each), a thread taking pieces t,
+    // t + 256, ... of its group; a piece whose two tags are current goes to
+    // LDS, otherwise its group stays pending for the next round.
+    {
+        typedef __attribute__((ext_vector_type(4))) u32 v4u;
+        const __amdgpu_buffer_rsrc_t hr = rsrc_of(hq, (uint64_t)NG * Imax * 8);
+        uint64_t pending = (NG >= 64) ? ~0ull : ((1ull << NG) - 1ull);
+        const int quarter = tid >> 8, qt = tid & 255;
+        for (u32 round = 0;; ++round) {
+            if (tid == 0) { S.stale[(round + 1) % 3][0] = 0u; S.stale[(round + 1) % 3][1] = 0u; }
+            if (round > 0) __builtin_amdgcn_s_sleep(1);
+            uint64_t stale = 0;
+            int j = 0;
+            for (uint64_t m = pending; m != 0; m &= m - 1, ++j) {
+                if ((j & 3) != quarter) continue;
+                const int g = __builtin_ctzll(m);
+                const int npc = ((g < k) ? I : Ish) / 2;   // 16-byte pieces of the group
+                constexpr int NB = 2;                       // pieces of one group per thread per batch
+                for (int b0 = 0; b0 < npc; b0 += 256 * NB) {
+                    v4u pc[NB];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const int pi = b0 + 256 * b + qt;
+                        const u32 off = (u32)(g * Imax * 8 + (pi < npc ? pi : 0) * 16);
+                        pc[b] = round == 0 ? __builtin_amdgcn_raw_buffer_load_b128(hr, (int)off, 0, 0)
+                                           : __builtin_amdgcn_raw_buffer_load_b128(hr, (int)off, 0, 16);   // sc1
+                    }
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const int pi = b0 + 256 * b + qt;
+                        if (pi < npc) {
+                            if (pc[b].y == tag && pc[b].w == tag) {
+                                // compact words 2m, 2m+1 of unit u: LDS piece (2m)/4 ^ swz(u), half m & 1
+                                const int u = pi >> 4, m2 = pi & 15;
+                                u32 *dstw = s_h + g * Imax + 32 * u + 4 * ((m2 >> 1) ^ d1_piece_swz(u)) + 2 * (m2 & 1);
+                                dstw[0] = pc[b].x;
+                                dstw[1] = pc[b].z;
+                            } else {
+                                stale |= 1ull << g;
+                            }
+                        }
+                    }
+                }
+            }
+            stale = (uint64_t)wave_or_u32((u32)stale) | ((uint64_t)wave_or_u32((u32)(stale >> 32)) << 32);
+            if (lane == 0 && stale != 0) {
+                __hip_atomic_fetch_or(&S.stale[round % 3][0], (u32)stale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_or(&S.stale[round % 3][1], (u32)(stale >> 32), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            ring_barrier();
+            pending = (uint64_t)S.stale[round % 3][0] | ((uint64_t)S.stale[round % 3][1] << 32);
+            if (pending == 0 && a.spin_limit != 0u) break;
+            // bounded; spin_limit 0 (the test hook) expires after one round
+            if (round >= a.spin_limit) {
+                if (tid == 0) d1_st_relaxed(&hdr[WS_ERR], 1u);
+                break;
+            }
+        }
+    }
+
+    // ---------------------------------------------- down dots
+#pragma unroll
+    for (int s = 0; s < MD; ++s) {
+        float acc = 0.f;
+        if (dn_g[s] >= 0) {
+            const int g = dn_g[s];
+            const int Ug = ((g < k) ? I : Ish) / 32;
 #pragma unroll
             for (int q = 0; q < QD; ++q) {
                 const int u = lrd + LPRd * q;
-                load_unit<FMT>(dn_un[s][q], c, sc, u < Ug ? u : lrd);
-            }
-        }
-        gu_dots();
-        ring_barrier();   // gate/up results in LDS (bare: the down rows may still be in flight)
-        ring_barrier();   // all of h in LDS
-
-        // ---------------------------------------------- down dots
+                if (u < Ug) {
+                    const uint4 *hb = reinterpret_cast<const uint4 *>(s_h + g * Imax + 32 * u);
+                    const int sw = d1_piece_swz(u);
+                    u32 xh[16], xl[16];
 #pragma unroll
-        for (int s = 0; s < MD; ++s) {
-            float acc = 0.f;
-            if (dn_g[s] >= 0) {
-                const int g = dn_g[s];
-                const int Ug = ((g < k) ? I : Ish) / 32;
-#pragma unroll
-                for (int q = 0; q < QD; ++q) {
-                    const int u = lrd + LPRd * q;
-                    if (u < Ug) {
-                        const uint4 *hb = reinterpret_cast<const uint4 *>(s_h + g * Imax + 32 * u);
-                        const int sw = d1_piece_swz(u);
-                        u32 xh[16], xl[16];
-#pragma unroll
-                        for (int vv = 0; vv < 4; ++vv) {
-                            const uint4 A = hb[vv ^ sw], B = hb[(4 + vv) ^ sw];
-                            xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
-                            xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
-                        }
-                        u32 wd[16];
-                        decode_unit<FMT, DEC>(dn_un[s][q], Lt, wd);
-                        float s0, s1;
-                        unit_scales<FMT>(dn_un[s][q], Lt, s0, s1);
-                        acc = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc);
+                    for (int vv = 0; vv < 4; ++vv) {
+                        const uint4 A = hb[vv ^ sw], B = hb[(4 + vv) ^ sw];
+                        xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
+                        xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
                     }
+                    u32 wd[16];
+                    decode_unit<FMT, DEC>(dn_un[s][q], Lt, wd);
+                    float s0, s1;
+                    unit_scales<FMT>(dn_un[s][q], Lt, s0, s1);
+                    acc = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc);
                 }
             }
-            acc = group_sum_dpp(acc, LPRd);
-            if (dn_g[s] >= 0 && lrd == 0) S.y[dn_g[s] * D1_MAX_RW + dn_r[s]] = acc;
         }
-    } else {
-        // ---------------------------------------------- exchange wave: gate/up dots, then the exchange
-        gu_dots();
-        ring_barrier();   // gate/up results in LDS
-        const u32 tag = S.tag;
-        // h of this workgroup's pairs as bf16 hi/lo pair words, in unit layout
-        if (2 * lane < n) {
-            const int j = 2 * lane;
-            const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
-            const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
-            const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
-            const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
-            const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-            const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
-            u32 *dst = hp + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
-            d1_st_relaxed(dst, hi0 | (hi1 << 16));
-            d1_st_relaxed(dst + 16, lo0 | (lo1 << 16));
-        }
-        wait_vm<0>();   // this wave has nothing else in flight: only the h stores are waited for
-        if (lane == 0) d1_st_relaxed(&flags[w], tag);
-
-        // poll every workgroup's flag; copy each expert group's h into LDS as
-        // soon as all of its producers are ready.  A workgroup's pairs span
-        // groups min(lo / I, k) .. min((hi - 1) / I, k).
-        typedef __attribute__((ext_vector_type(4))) u32 v4u;
-        const int G = plan.G;
-        const __amdgpu_buffer_rsrc_t fr = rsrc_of(flags, (uint64_t)G * 4);
-        const __amdgpu_buffer_rsrc_t hr = rsrc_of(hp, (uint64_t)NG * Imax * 4);
-        uint64_t pending = (NG >= 64) ? ~0ull : ((1ull << NG) - 1ull);
-        u32 spins = 0;
-        for (;;) {
-            uint64_t notready = 0;
-            for (int c = 0; c < G; c += 256) {
-                const int w0 = c + 4 * lane;
-                const v4u f = __builtin_amdgcn_raw_buffer_load_b128(fr, w0 * 4, 0, 16);   // sc1
-                const u32 fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int wi = w0 + i;
-                    if (wi < G && fv[i] != tag) {
-                        const int lo = d1_pair_lo(plan.P, G, wi), hi = d1_pair_lo(plan.P, G, wi + 1);
-                        const int g0 = min(lo / I, k), g1 = min((hi - 1) / I, k);
-                        notready |= ((2ull << g1) - 1ull) & ~((1ull << g0) - 1ull);
-                    }
-                }
-            }
-            notready = (uint64_t)wave_or_u32((u32)notready) | ((uint64_t)wave_or_u32((u32)(notready >> 32)) << 32);
-            const uint64_t ready = pending & ~notready;
-            for (uint64_t m = ready; m != 0; m &= m - 1) {
-                const int g = __builtin_ctzll(m);
-                const int npc = ((g < k) ? I : Ish) / 4;   // 16-byte pieces of the group's h
-                for (int p0 = 0; p0 < npc; p0 += 64) {
-                    const int p = p0 + lane;
-                    if (p < npc) {
-                        // LDS piece p = (unit p/8, slot p%8) takes piece slot ^ swz(unit) of that unit
-                        const int u = p >> 3, src = (u << 3) | ((p & 7) ^ d1_piece_swz(u));
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (lds_void_t *)(s_h + g * Imax + 4 * p0), 16,
-                                                                 (u32)((g * Imax) * 4 + src * 16), 0, 0, 16);
-                    }
-                }
-            }
-            pending &= ~ready;
-            if (pending == 0 && a.spin_limit != 0u) break;
-            // bounded; spin_limit 0 (the test hook) expires at once
-            if (spins++ >= a.spin_limit) { d1_st_relaxed(&hdr[WS_ERR], 1u); break; }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        wait_vm<0>();
-        ring_barrier();   // all of h in LDS
+        acc = group_sum_dpp(acc, LPRd);
+        if (dn_g[s] >= 0 && lrd == 0) S.y[dn_g[s] * D1_MAX_RW + dn_r[s]] = acc;
     }
     __syncthreads();
     for (int r = tid; r < nr; r += D1_THREADS) {
@@ -400,16 +406,15 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
     int G = cus;
     if (G > P / 16) G = P / 16;
     if (G > cap) G = cap;
-    if (G > D1_MAX_WGS) G = D1_MAX_WGS;
     if (G < 1) return hipErrorNotSupported;
     int nmax = 0;   // the largest pair range
     for (int w = 0; w < G; ++w) nmax = std::max(nmax, d1_pair_lo(P, G, w + 1) - d1_pair_lo(P, G, w));
     if (nmax > D1_MAX_PAIRS_WG || 2 * nmax > D1_NW * MG * RPWg) return hipErrorNotSupported;
     const int rw = (L.H + G - 1) / G;
-    if (rw > D1_MAX_RW || NG * rw > D1_XW * MD * RPWd) return hipErrorNotSupported;
+    if (rw > D1_MAX_RW || NG * rw > D1_NW * MD * RPWd) return hipErrorNotSupported;
     // floor(2^32 / rw) + 1: exact quotients for the small numerators used (checked)
     D1Plan plan{G, P, rw, (1ull << 32) / (uint64_t)rw + 1u, down_lanes_per_row(L.I, L.Ish)};
-    for (int v = 0; v < (D1_XW * MD + D1_NW) * RPWd; ++v)
+    for (int v = 0; v < D1_NW * (MD + 1) * RPWd; ++v)
         if ((int)(((uint64_t)v * plan.magic_rw) >> 32) != v / rw) return hipErrorNotSupported;
     hipLaunchKernelGGL(kern, dim3(G), dim3(D1_THREADS), dyn, s, a, plan);
     return hipGetLastError();

@@ -49,7 +49,6 @@ constexpr int DEC_MAX_PAIRS = DEC_MAX_T * 33;
 constexpr int DEC_MAX_DIM = 8192;  // H, I, Ish on the decode path (x/h held in registers)
 constexpr int DEC_S1 = 16;         // I-rows (gate and up) per gate/up item
 constexpr int DEC_S2 = 64;         // output rows per down item
-constexpr int D1_MAX_WGS = 4096;   // single-token kernel: workgroups (one ready flag each)
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k);
 
