@@ -13,12 +13,13 @@
 //   down      : workgroup w computes RW consecutive output rows for EVERY
 //               selected expert and combines them itself, in rank order, so no
 //               partial sums leave the CU.
-// Each workgroup routes the token itself, then issues all of its weight loads
-// at once (gate/up rows, then down rows, into registers), so the whole layer
-// is in flight after one routing delay.  Every load is issued
-// unconditionally (idle slots re-load a row the workgroup loads anyway), so
-// the compiler counts outstanding loads exactly and the gate/up dots wait for
-// the gate/up rows only, not for the down rows behind them.
+// Each workgroup routes the token itself, then issues all of its gate/up
+// loads at once (into registers).  Its down rows are issued right after it
+// has published its h and started reading everyone's: h is on the critical
+// path, the down rows are not needed before all of h is in, and requests
+// queue in issue order.  Every load is issued unconditionally (idle slots
+// re-load a row the workgroup loads anyway), so the compiler counts
+// outstanding loads exactly and waits only for the ones it needs.
 //
 //
 // The down rows need every expert's h.  One wave of each workgroup publishes
@@ -60,7 +61,8 @@ __device__ inline u32 wave_or_u32(u32 v) {
 
 constexpr int D1_NW = 16;                  // waves per workgroup
 constexpr int D1_THREADS = 64 * D1_NW;
-constexpr int D1_MAX_PAIRS_WG = 128;       // gate/up pairs per workgroup (two per lane of the exchange wave)
+constexpr int D1_MAX_PAIRS_WG = 128;       // gate/up pairs per workgroup (two per lane of the publishing wave)
+constexpr int D1_NB0 = 4;                  // first pass over h: 16-byte pieces per thread
 
 struct D1Plan {
     int G;              // workgroups
@@ -214,7 +216,54 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     const int o0 = w * plan.rw;
     const int nr = max(0, min(H, o0 + plan.rw) - o0);
 
-    // ---------------------------------------------- down rows in flight (every wave)
+    // ---------------------------------------------- gate | up dots, h published
+    gu_dots();
+    ring_barrier();   // gate/up results in LDS
+    const u32 tag = S.tag;
+    if (wv == D1_NW - 1 && 2 * lane < n) {
+        const int j = 2 * lane;
+        const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
+        const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
+        const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
+        const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
+        const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
+        const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
+        uint64_t *dst = hq + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
+        __hip_atomic_store(dst, ((uint64_t)tag << 32) | (hi0 | (hi1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 16, ((uint64_t)tag << 32) | (lo0 | (lo1 << 16)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---------------------------------------------- first pass over all of h, then the down rows
+    // Group g's words are Ig/2 16-byte pieces (two words each: compact words
+    // 2m, 2m+1 of its unit layout), at piece slots g*Imax/2 ...  The first pass
+    // reads every slot once (D1_NB0 pieces per thread, ordinary loads: the
+    // workgroups of an XCD share the lines through its L2); a piece whose two
+    // tags are current goes to LDS, otherwise its group is read again.  The
+    // down rows are issued after the first pass: h is on the critical path,
+    // the down rows are not needed before it is complete.
+    typedef __attribute__((ext_vector_type(4))) u32 v4u;
+    const __amdgpu_buffer_rsrc_t hr = rsrc_of(hq, (uint64_t)NG * Imax * 8);
+    const int slot_pc = Imax / 2;
+    auto keep_piece = [&](int g, int pi, const v4u &pc, uint64_t &stale) {
+        if (pc.y == tag && pc.w == tag) {
+            // compact words 2m, 2m+1 of unit u: LDS piece (2m)/4 ^ swz(u), half m & 1
+            const int u = pi >> 4, m2 = pi & 15;
+            u32 *dstw = s_h + g * Imax + 32 * u + 4 * ((m2 >> 1) ^ d1_piece_swz(u)) + 2 * (m2 & 1);
+            dstw[0] = pc.x;
+            dstw[1] = pc.z;
+        } else {
+            stale |= 1ull << g;
+        }
+    };
+    v4u pc0[D1_NB0];
+#pragma unroll
+    for (int b = 0; b < D1_NB0; ++b) {
+        const int q = tid + D1_THREADS * b, g = q / slot_pc, pi = q - g * slot_pc;
+        const bool ok = g < NG && pi < ((g < k) ? I : Ish) / 2;
+        pc0[b] = __builtin_amdgcn_raw_buffer_load_b128(hr, ok ? (int)(g * Imax * 8 + pi * 16) : 0, 0, 0);
+    }
+
     const int LPRd = plan.lpr_d, RPWd = WAVE / LPRd;
     const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
     int dn_g[MD], dn_r[MD];
@@ -242,68 +291,57 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
         }
     }
 
-    // ---------------------------------------------- gate | up dots, h published
-    gu_dots();
-    ring_barrier();   // gate/up results in LDS (bare: the down rows may still be in flight)
-    const u32 tag = S.tag;
-    if (wv == D1_NW - 1 && 2 * lane < n) {
-        const int j = 2 * lane;
-        const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
-        const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
-        const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
-        const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
-        const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-        const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
-        uint64_t *dst = hq + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
-        __hip_atomic_store(dst, ((uint64_t)tag << 32) | (hi0 | (hi1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 16, ((uint64_t)tag << 32) | (lo0 | (lo1 << 16)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // ---------------------------------------------- gather all of h (every wave)
-    // Group g's words are Ig/2 16-byte pieces (two words each: compact words
-    // 2m, 2m+1 of its unit layout).  Pending groups are dealt to quarters of
-    // the workgroup in turn (256 threads each), a thread taking pieces t,
-    // t + 256, ... of its group; a piece whose two tags are current goes to
-    // LDS, otherwise its group stays pending for the next round.
     {
-        typedef __attribute__((ext_vector_type(4))) u32 v4u;
-        const __amdgpu_buffer_rsrc_t hr = rsrc_of(hq, (uint64_t)NG * Imax * 8);
-        uint64_t pending = (NG >= 64) ? ~0ull : ((1ull << NG) - 1ull);
+        uint64_t stale = 0;
+#pragma unroll
+        for (int b = 0; b < D1_NB0; ++b) {
+            const int q = tid + D1_THREADS * b, g = q / slot_pc, pi = q - g * slot_pc;
+            if (g < NG && pi < ((g < k) ? I : Ish) / 2) keep_piece(g, pi, pc0[b], stale);
+        }
+        stale = (uint64_t)wave_or_u32((u32)stale) | ((uint64_t)wave_or_u32((u32)(stale >> 32)) << 32);
+        if (lane == 0 && stale != 0) {
+            __hip_atomic_fetch_or(&S.stale[0][0], (u32)stale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_or(&S.stale[0][1], (u32)(stale >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    ring_barrier();
+
+    // ---------------------------------------------- further passes, device-coherent, over the stale groups
+    // Pending groups are dealt to quarters of the workgroup in turn (256
+    // threads each), a thread taking pieces t, t + 256, ... of its group.
+    {
+        uint64_t pending = (uint64_t)S.stale[0][0] | ((uint64_t)S.stale[0][1] << 32);
+        if (a.spin_limit == 0u) {   // the test hook: the bounded wait expires at once
+            if (tid == 0) d1_st_relaxed(&hdr[WS_ERR], 1u);
+            pending = 0;
+        }
         const int quarter = tid >> 8, qt = tid & 255;
-        for (u32 round = 0;; ++round) {
+        for (u32 round = 1; pending != 0; ++round) {
+            if (round > a.spin_limit) {
+                if (tid == 0) d1_st_relaxed(&hdr[WS_ERR], 1u);
+                break;
+            }
             if (tid == 0) { S.stale[(round + 1) % 3][0] = 0u; S.stale[(round + 1) % 3][1] = 0u; }
-            if (round > 0) __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(1);
             uint64_t stale = 0;
             int j = 0;
             for (uint64_t m = pending; m != 0; m &= m - 1, ++j) {
                 if ((j & 3) != quarter) continue;
                 const int g = __builtin_ctzll(m);
-                const int npc = ((g < k) ? I : Ish) / 2;   // 16-byte pieces of the group
-                constexpr int NB = 2;                       // pieces of one group per thread per batch
+                const int npc = ((g < k) ? I : Ish) / 2;
+                constexpr int NB = 2;
                 for (int b0 = 0; b0 < npc; b0 += 256 * NB) {
                     v4u pc[NB];
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const int pi = b0 + 256 * b + qt;
-                        const u32 off = (u32)(g * Imax * 8 + (pi < npc ? pi : 0) * 16);
-                        pc[b] = round == 0 ? __builtin_amdgcn_raw_buffer_load_b128(hr, (int)off, 0, 0)
-                                           : __builtin_amdgcn_raw_buffer_load_b128(hr, (int)off, 0, 16);   // sc1
+                        pc[b] = __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(g * Imax * 8 + (pi < npc ? pi : 0) * 16),
+                                                                     0, 16);   // sc1
                     }
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         const int pi = b0 + 256 * b + qt;
-                        if (pi < npc) {
-                            if (pc[b].y == tag && pc[b].w == tag) {
-                                // compact words 2m, 2m+1 of unit u: LDS piece (2m)/4 ^ swz(u), half m & 1
-                                const int u = pi >> 4, m2 = pi & 15;
-                                u32 *dstw = s_h + g * Imax + 32 * u + 4 * ((m2 >> 1) ^ d1_piece_swz(u)) + 2 * (m2 & 1);
-                                dstw[0] = pc[b].x;
-                                dstw[1] = pc[b].z;
-                            } else {
-                                stale |= 1ull << g;
-                            }
-                        }
+                        if (pi < npc) keep_piece(g, pi, pc[b], stale);
                     }
                 }
             }
@@ -315,12 +353,6 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
             }
             ring_barrier();
             pending = (uint64_t)S.stale[round % 3][0] | ((uint64_t)S.stale[round % 3][1] << 32);
-            if (pending == 0 && a.spin_limit != 0u) break;
-            // bounded; spin_limit 0 (the test hook) expires after one round
-            if (round >= a.spin_limit) {
-                if (tid == 0) d1_st_relaxed(&hdr[WS_ERR], 1u);
-                break;
-            }
         }
     }
 
@@ -358,6 +390,7 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     __syncthreads();
     for (int r = tid; r < nr; r += D1_THREADS) {
         float acc = 0.f;
+#pragma unroll 8
         for (int g = 0; g < k; ++g) acc = __builtin_fmaf(S.wsel[g], S.y[g * D1_MAX_RW + r], acc);
         if (Ish > 0) acc += S.y[k * D1_MAX_RW + r];
         if (a.out_f32) reinterpret_cast<float *>(a.out)[o0 + r] = acc;
@@ -435,7 +468,8 @@ hipError_t decode1_fd(const DecodeArgs &a, hipStream_t s) {
     if (a.T != 1 || a.mode != MODE_ROUTE) return hipErrorNotSupported;
     const int NG = L.k + (L.Ish > 0 ? 1 : 0);
     const int Imax = L.I > L.Ish ? L.I : L.Ish;
-    if (NG > D1_MAX_GROUPS || NG * Imax > D1_H_LDS_WORDS) return hipErrorNotSupported;
+    if (NG > D1_MAX_GROUPS || NG * Imax > D1_H_LDS_WORDS || NG * Imax / 2 > D1_NB0 * D1_THREADS)
+        return hipErrorNotSupported;
     const int UH = L.H / 32, LPRg = lanes_per_row(UH), QG = (UH + LPRg - 1) / LPRg;
     const int LPRd = down_lanes_per_row(L.I, L.Ish), QD = (Imax / 32 + LPRd - 1) / LPRd;
     if (QG == 1 && QD == 1) return decode1_q<FMT, DEC, 1, 1>(a, s);
