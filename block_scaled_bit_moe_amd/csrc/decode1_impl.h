@@ -22,10 +22,11 @@
 // outstanding loads exactly and waits only for the ones it needs.
 //
 //
-// The down rows need every expert's h.  One wave of each workgroup publishes
-// the workgroup's h as 64-bit words, each a bf16 hi or lo pair tagged with the
-// call tag in its upper half, with device-coherent stores (no wait: every
-// word carries its own tag, so no ordering between words is needed).  Then
+// The down rows need every expert's h.  The gate and up rows of a pair sit in
+// two slots of the same lane group, so that group's first lane has both dots
+// and publishes h of the pair at once, as a 64-bit word (call tag << 32 |
+// fp32 bits) with a device-coherent store: no barrier and no wait (every word
+// carries its own tag, so no ordering between words is needed).  Then
 // all 16 waves fetch every expert group's words, keep the payload of those
 // whose tag is current (into LDS, compact and swizzled) and fetch again the
 // groups that had a stale word, until all are in.  The first fetch uses
@@ -61,7 +62,7 @@ __device__ inline u32 wave_or_u32(u32 v) {
 
 constexpr int D1_NW = 16;                  // waves per workgroup
 constexpr int D1_THREADS = 64 * D1_NW;
-constexpr int D1_MAX_PAIRS_WG = 128;       // gate/up pairs per workgroup (two per lane of the publishing wave)
+constexpr int D1_MAX_PAIRS_WG = 1024;      // gate/up pairs per workgroup
 constexpr int D1_NB0 = 4;                  // first pass over h: 16-byte pieces per thread
 
 struct D1Plan {
@@ -85,13 +86,11 @@ struct D1Shared {
     float wsel[D1_MAX_GROUPS];      // its gate weight (1 for the shared expert)
     u32 tag;
     u32 stale[3][2];                // per fetch round (mod 3): groups with a stale word
-    float gu[2 * D1_MAX_PAIRS_WG];  // gate/up dot results of this workgroup
     float y[D1_MAX_GROUPS * D1_MAX_RW];   // down results: [group][local row]
 };
 
-// Region of the workspace for this kernel: h as [group][Imax] 64-bit words in
-// unit layout (unit u of 32 elements: 16 words of bf16 hi pairs, then 16 words
-// of lo pairs), each word (call tag << 32) | pair.
+// Region of the workspace for this kernel: h as [group][Imax] 64-bit words,
+// word i = (call tag << 32) | fp32 bits of h_i.
 __host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * 4 + (size_t)DEC_MAX_PAIRS * H * 4;
@@ -169,35 +168,43 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     __syncthreads();
 
     // ------------------------------------------------ gate/up rows of this workgroup's pairs
-    // row task t < 2n: t < n is the gate row of pair pl + t, else the up row of pair pl + t - n;
-    // pair p belongs to group min(p / I, k) (routed experts in rank order, then the shared one)
-    const int w = blockIdx.x, kI = k * I;
+    // slot s of a lane group holds pair j = (wave + 16 * (s / 2)) * RPWg + group,
+    // its gate row in even slots and its up row in odd ones; pair pl + j belongs
+    // to group min(p / I, k) (routed experts in rank order, then the shared one)
+    const int w = blockIdx.x;
     const int pl = d1_pair_lo(plan.P, plan.G, w), n = d1_pair_lo(plan.P, plan.G, w + 1) - pl;
+    static_assert(MG % 2 == 0, "gate and up slots come in pairs");
     Unit<FMT> gu_un[MG][QG];
-    int gu_task[MG];
 #pragma unroll
     for (int s = 0; s < MG; ++s) {
-        const int t = (wv + D1_NW * s) * RPWg + rsg;
-        gu_task[s] = t < 2 * n ? t : -1;
-        const int tc = t < 2 * n ? t : 0;   // idle slots re-load task 0
-        const int p = pl + (tc < n ? tc : tc - n);
+        const int j = (wv + D1_NW * (s >> 1)) * RPWg + rsg;
+        const int p = pl + (j < n ? j : 0);   // idle slots re-load pair 0
         const int g = min(p / I, k);
         const int i = p - g * I;
-        const int e = g < k ? S.sel[g] : -1;
-        const int Ig = g < k ? I : Ish;
-        const int row = tc < n ? i : Ig + i;
-        const uint8_t *c = (e >= 0 ? ly.w13c + (int64_t)e * 2 * I * crbH : ly.sh13c) + (int64_t)row * crbH;
-        const uint8_t *sc = (e >= 0 ? ly.w13s + (int64_t)e * 2 * I * srbH : ly.sh13s) + (int64_t)row * srbH;
+        const int e = S.sel[g];
+        const int row = (s & 1) ? ((g < k) ? I : Ish) + i : i;
+        // branch-free address selection (a branch here makes the compiler wait for loads in flight)
+        const int64_t er = (int64_t)max(e, 0) * 2 * I + row;
+        const uint8_t *c = (e >= 0 ? ly.w13c + er * crbH : ly.sh13c + (int64_t)row * crbH);
+        const uint8_t *sc = (e >= 0 ? ly.w13s + er * srbH : ly.sh13s + (int64_t)row * srbH);
 #pragma unroll
         for (int q = 0; q < QG; ++q) {
             const int u = lrg + LPRg * q;
             load_unit<FMT>(gu_un[s][q], c, sc, u < UH ? u : lrg);
         }
     }
-    auto gu_dots = [&]() {
+    const int o0 = w * plan.rw;
+    const int nr = max(0, min(H, o0 + plan.rw) - o0);
+
+    // ---------------------------------------------- gate | up dots; each pair's h published at once
+    const u32 tag = S.tag;
 #pragma unroll
-        for (int s = 0; s < MG; ++s) {
-            float acc = 0.f;
+    for (int s2 = 0; s2 < MG / 2; ++s2) {
+        float acc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = 2 * s2 + h;
+            acc[h] = 0.f;
 #pragma unroll
             for (int q = 0; q < QG; ++q) {
                 const int u = lrg + LPRg * q;
@@ -206,37 +213,24 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
                     decode_unit<FMT, DEC>(gu_un[s][q], Lt, wd);
                     float s0, s1;
                     unit_scales<FMT>(gu_un[s][q], Lt, s0, s1);
-                    acc = unit_dot<FMT>(wd, xr[q][0], s0, s1, acc);
+                    acc[h] = unit_dot<FMT>(wd, xr[q][0], s0, s1, acc[h]);
                 }
             }
-            acc = group_sum_dpp(acc, LPRg);
-            if (gu_task[s] >= 0 && lrg == 0) S.gu[gu_task[s]] = acc;
+            acc[h] = group_sum_dpp(acc[h], LPRg);
         }
-    };
-    const int o0 = w * plan.rw;
-    const int nr = max(0, min(H, o0 + plan.rw) - o0);
-
-    // ---------------------------------------------- gate | up dots, h published
-    gu_dots();
-    ring_barrier();   // gate/up results in LDS
-    const u32 tag = S.tag;
-    if (wv == D1_NW - 1 && 2 * lane < n) {
-        const int j = 2 * lane;
-        const float h0 = silu_f32(S.gu[j]) * S.gu[n + j];
-        const float h1 = silu_f32(S.gu[j + 1]) * S.gu[n + j + 1];
-        const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
-        const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
-        const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
-        const int p = pl + j, g = min(p / I, k), e0 = p - g * I;
-        uint64_t *dst = hq + (size_t)g * Imax + 32 * (e0 >> 5) + ((e0 & 31) >> 1);
-        __hip_atomic_store(dst, ((uint64_t)tag << 32) | (hi0 | (hi1 << 16)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 16, ((uint64_t)tag << 32) | (lo0 | (lo1 << 16)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const int j = (wv + D1_NW * s2) * RPWg + rsg;
+        if (j < n && lrg == 0) {
+            const float hv = silu_f32(acc[0]) * acc[1];
+            const int p = pl + j, g = min(p / I, k), i = p - g * I;
+            __hip_atomic_store(hq + (size_t)g * Imax + i, ((uint64_t)tag << 32) | __builtin_bit_cast(u32, hv),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
+    ring_barrier();   // this workgroup's h is published
 
     // ---------------------------------------------- first pass over all of h, then the down rows
-    // Group g's words are Ig/2 16-byte pieces (two words each: compact words
-    // 2m, 2m+1 of its unit layout), at piece slots g*Imax/2 ...  The first pass
+    // Group g's words are Ig/2 16-byte pieces (two elements each), at piece
+    // slots g*Imax/2 ...  The first pass
     // reads every slot once (D1_NB0 pieces per thread, ordinary loads: the
     // workgroups of an XCD share the lines through its L2); a piece whose two
     // tags are current goes to LDS, otherwise its group is read again.  The
@@ -247,11 +241,19 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     const int slot_pc = Imax / 2;
     auto keep_piece = [&](int g, int pi, const v4u &pc, uint64_t &stale) {
         if (pc.y == tag && pc.w == tag) {
-            // compact words 2m, 2m+1 of unit u: LDS piece (2m)/4 ^ swz(u), half m & 1
-            const int u = pi >> 4, m2 = pi & 15;
-            u32 *dstw = s_h + g * Imax + 32 * u + 4 * ((m2 >> 1) ^ d1_piece_swz(u)) + 2 * (m2 & 1);
-            dstw[0] = pc.x;
-            dstw[1] = pc.z;
+            // elements 2*pi, 2*pi + 1: their bf16 hi pair and lo pair words go to
+            // unit u = pi / 16, pair pe = pi % 16 (hi in pieces 0..3, lo in 4..7, swizzled)
+            // (components copied to scalars first: this compiler reads component 0
+            // for a __builtin_bit_cast of a vector component)
+            const u32 b0 = pc.x, b1 = pc.z;
+            const float h0 = __builtin_bit_cast(float, b0), h1 = __builtin_bit_cast(float, b1);
+            const u32 hi0 = f32_to_bf16_rne(h0), hi1 = f32_to_bf16_rne(h1);
+            const u32 lo0 = f32_to_bf16_rne(h0 - __builtin_bit_cast(float, hi0 << 16));
+            const u32 lo1 = f32_to_bf16_rne(h1 - __builtin_bit_cast(float, hi1 << 16));
+            const int u = pi >> 4, pe = pi & 15, sw = d1_piece_swz(u);
+            u32 *ub = s_h + g * Imax + 32 * u + (pe & 3);
+            ub[4 * ((pe >> 2) ^ sw)] = hi0 | (hi1 << 16);
+            ub[4 * ((4 + (pe >> 2)) ^ sw)] = lo0 | (lo1 << 16);
         } else {
             stale |= 1ull << g;
         }
@@ -281,8 +283,9 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
         const int e = S.sel[ok ? g : 0], o = min(o0 + dn_r[s], H - 1);
         const int Ig = (e >= 0) ? I : Ish;
         const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
-        const uint8_t *c = (e >= 0) ? ly.w2c + ((int64_t)e * H + o) * crbI : ly.sh2c + (int64_t)o * crbI;
-        const uint8_t *sc = (e >= 0) ? ly.w2s + ((int64_t)e * H + o) * srbI : ly.sh2s + (int64_t)o * srbI;
+        const int64_t eo = (int64_t)max(e, 0) * H + o;   // branch-free, as for the gate/up rows
+        const uint8_t *c = (e >= 0) ? ly.w2c + eo * crbI : ly.sh2c + (int64_t)o * crbI;
+        const uint8_t *sc = (e >= 0) ? ly.w2s + eo * srbI : ly.sh2s + (int64_t)o * srbI;
         const int Ug = Ig / 32;
 #pragma unroll
         for (int q = 0; q < QD; ++q) {
@@ -442,7 +445,7 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
     if (G < 1) return hipErrorNotSupported;
     int nmax = 0;   // the largest pair range
     for (int w = 0; w < G; ++w) nmax = std::max(nmax, d1_pair_lo(P, G, w + 1) - d1_pair_lo(P, G, w));
-    if (nmax > D1_MAX_PAIRS_WG || 2 * nmax > D1_NW * MG * RPWg) return hipErrorNotSupported;
+    if (nmax > D1_MAX_PAIRS_WG || nmax > D1_NW * (MG / 2) * RPWg) return hipErrorNotSupported;
     const int rw = (L.H + G - 1) / G;
     if (rw > D1_MAX_RW || NG * rw > D1_NW * MD * RPWd) return hipErrorNotSupported;
     // floor(2^32 / rw) + 1: exact quotients for the small numerators used (checked)
@@ -455,9 +458,9 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
 
 template <int FMT, int DEC, int QG, int QD>
 static hipError_t decode1_q(const DecodeArgs &a, hipStream_t s) {
-    hipError_t e = decode1_try<FMT, DEC, QG, QD, 1, 1>(a, s);
+    hipError_t e = decode1_try<FMT, DEC, QG, QD, 2, 1>(a, s);
     if (e != hipErrorNotSupported) return e;
-    e = decode1_try<FMT, DEC, QG, QD, 3, 2>(a, s);
+    e = decode1_try<FMT, DEC, QG, QD, 4, 2>(a, s);
     if (e != hipErrorNotSupported) return e;
     return decode1_try<FMT, DEC, QG, QD, 8, 4>(a, s);
 }
