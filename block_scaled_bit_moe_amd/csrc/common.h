@@ -337,17 +337,9 @@ __device__ inline void route_load_logits(const float *__restrict__ logits, int E
     for (int j = 0; j < PER_LANE; ++j) lg[j] = logits[min(lane * PER_LANE + j, E - 1)];   // all loads in flight
 }
 
+// Per-lane bitonic sort of PER_LANE unique 64-bit keys, descending.
 template <int PER_LANE>
-__device__ inline void route_from_logits(const float (&lg)[PER_LANE], int E, int k, int lane, int &my_idx,
-                                         float &my_w) {
-    uint64_t key[PER_LANE];
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-        const int e = lane * PER_LANE + j;
-        const u32 lk = (e < E) ? logit_key(lg[j]) : 0u;   // 0: no expert, below NaN (1)
-        key[j] = ((uint64_t)lk << 32) | (u32)~(u32)e;
-    }
-    // bitonic sort, descending
+__device__ inline void sort_keys_desc(uint64_t (&key)[PER_LANE]) {
 #pragma unroll
     for (int sz = 2; sz <= PER_LANE; sz <<= 1)
 #pragma unroll
@@ -363,11 +355,22 @@ __device__ inline void route_from_logits(const float (&lg)[PER_LANE], int E, int
                     key[l] = sw ? a : b;
                 }
             }
-    my_idx = -1;
-    float my_l = 0.f, l0 = 0.f;
+}
+
+// Unique routing key of expert e with logit v: the order key of the logit in
+// the high half, the complement of the index in the low half (0: no expert).
+__device__ inline uint64_t expert_key(float v, int e, bool valid) {
+    return ((uint64_t)(valid ? logit_key(v) : 0u) << 32) | (u32)~(u32)e;
+}
+
+// k rounds over per-lane lists sorted descending: round r takes the wave-wide
+// largest first key (its logit half, then among the lanes holding that logit
+// its index half) and the lane holding it drops it.  Lane r ends with the key
+// of rank r (lanes >= k: 0).
+template <int PER_LANE>
+__device__ inline uint64_t topk_rounds(uint64_t (&key)[PER_LANE], int k, int lane) {
+    uint64_t mine = 0;
     for (int r = 0; r < k; ++r) {
-        // the largest first key: its logit half first, then (among the lanes
-        // holding that logit, if more than one) its index half
         const u32 hv = (u32)(key[0] >> 32), hl = (u32)key[0];
         const u32 mv = wave_max_u32(hv);
         const uint64_t holders = __ballot(hv == mv);
@@ -380,16 +383,35 @@ __device__ inline void route_from_logits(const float (&lg)[PER_LANE], int E, int
 #pragma unroll
         for (int j = 0; j + 1 < PER_LANE; ++j) key[j] = win ? key[j + 1] : key[j];
         if (win) key[PER_LANE - 1] = 0u;
-        const int e = (int)~ml;
-        const float lv = logit_of_key(mv);
-        if (r == 0) l0 = lv;
-        if (lane == r) { my_idx = e; my_l = lv; }
+        if (lane == r) mine = ((uint64_t)mv << 32) | ml;
     }
-    // weights: exp(l_r - l_0) / sum over the k picks (fp32, fixed order r = 0..k-1)
+    return mine;
+}
+
+// Lanes 0 .. k-1 hold the keys of ranks 0 .. k-1: their experts and the
+// softmax over the k picked logits in fp32, exp(l_r - l_0) summed in rank order.
+__device__ inline void weights_from_ranked(uint64_t mine, int k, int lane, int &my_idx, float &my_w) {
+    const float my_l = logit_of_key((u32)(mine >> 32));
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), 0));
+    my_idx = (lane < k) ? (int)~(u32)mine : -1;
     const float ex = (lane < k) ? expf(my_l - l0) : 0.f;
     float z = 0.f;
     for (int r = 0; r < k; ++r) z += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), r));
     my_w = (lane < k) ? ex / z : 0.f;
+}
+
+template <int PER_LANE>
+__device__ inline void route_from_logits(const float (&lg)[PER_LANE], int E, int k, int lane, int &my_idx,
+                                         float &my_w) {
+    uint64_t key[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+        const int e = lane * PER_LANE + j;
+        key[j] = expert_key(lg[j], e, e < E);
+    }
+    sort_keys_desc<PER_LANE>(key);
+    const uint64_t mine = topk_rounds<PER_LANE>(key, k, lane);
+    weights_from_ranked(mine, k, lane, my_idx, my_w);
 }
 
 template <int PER_LANE>

@@ -13,8 +13,9 @@
 //   down      : workgroup w computes RW consecutive output rows for EVERY
 //               selected expert and combines them itself, in rank order, so no
 //               partial sums leave the CU.
-// Each workgroup routes the token itself, then issues all of its gate/up
-// loads at once (into registers).  Its down rows are issued right after it
+// Each workgroup routes the token itself (by ranks: every key compared with
+// the others in parallel, no serial selection rounds), then issues all of its
+// gate/up loads at once (into registers).  Its down rows are issued right after it
 // has published its h and started reading everyone's: h is on the critical
 // path, the down rows are not needed before all of h is in, and requests
 // queue in issue order.  Every load is issued unconditionally (idle slots
@@ -64,6 +65,7 @@ constexpr int D1_NW = 16;                  // waves per workgroup
 constexpr int D1_THREADS = 64 * D1_NW;
 constexpr int D1_MAX_PAIRS_WG = 1024;      // gate/up pairs per workgroup
 constexpr int D1_NB0 = 4;                  // first pass over h: 16-byte pieces per thread
+constexpr int D1_MAX_LISTS = D1_NW;        // routing: experts E <= 64 * D1_MAX_LISTS
 
 struct D1Plan {
     int G;              // workgroups
@@ -86,6 +88,9 @@ struct D1Shared {
     float wsel[D1_MAX_GROUPS];      // its gate weight (1 for the shared expert)
     u32 tag;
     u32 stale[3][2];                // per fetch round (mod 3): groups with a stale word
+    __attribute__((aligned(16))) uint64_t lkey[D1_MAX_LISTS][64];   // routing: every expert's key, per wave
+    __attribute__((aligned(16))) uint64_t cand[D1_MAX_LISTS * 32];  // routing: each wave's top-k keys
+    uint64_t ranked[32];                // routing: the top-k keys in rank order
     float y[D1_MAX_GROUPS * D1_MAX_RW];   // down results: [group][local row]
 };
 
@@ -94,6 +99,36 @@ struct D1Shared {
 __host__ __device__ inline size_t d1_h_offset(int H, int I, int Ish) {
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * 4 + (size_t)DEC_MAX_PAIRS * H * 4;
+}
+
+// Number of the N keys at p (LDS, 16-byte aligned) larger than key: all N/2
+// 16-byte reads issued before any compare (every lane reads the same address).
+template <int N>
+__device__ inline int d1_count_greater(const uint64_t *p, uint64_t key) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    uint4 v[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] = q[i];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const uint64_t a = ((uint64_t)v[i].y << 32) | v[i].x, b = ((uint64_t)v[i].w << 32) | v[i].z;
+        c += (a > key) + (b > key);
+    }
+    return c;
+}
+
+// Number of the n (even) keys at p (LDS, 16-byte aligned) larger than key.
+__device__ inline int d1_count_greater_list(const uint64_t *p, int n, uint64_t key) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    int c = 0;
+#pragma unroll 8
+    for (int i = 0; i < n / 2; ++i) {
+        const uint4 v = q[i];
+        const uint64_t a = ((uint64_t)v.y << 32) | v.x, b = ((uint64_t)v.w << 32) | v.z;
+        c += (a > key) + (b > key);
+    }
+    return c;
 }
 
 // LDS layout of h: the 8 16-byte pieces of unit u are stored rotated by
@@ -119,19 +154,11 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
     uint64_t *hq = reinterpret_cast<uint64_t *>(a.ws + d1_h_offset(H, I, Ish));
     const int64_t crbH = Fmt<FMT>::code_row_bytes(H), srbH = Fmt<FMT>::scale_row_bytes(H);
 
-    // call tag, activation units and the routing logits are all fetched at once;
-    // the routing wave issues its logit loads first of all
-    float lgt[16];
-    if (wv == 0) {
-        if (E <= 64) route_load_logits<1>(a.logits, E, lane, reinterpret_cast<float(&)[1]>(lgt));
-        else if (E <= 128) route_load_logits<2>(a.logits, E, lane, reinterpret_cast<float(&)[2]>(lgt));
-        else if (E <= 256) route_load_logits<4>(a.logits, E, lane, reinterpret_cast<float(&)[4]>(lgt));
-        else if (E <= 512) route_load_logits<8>(a.logits, E, lane, reinterpret_cast<float(&)[8]>(lgt));
-        else route_load_logits<16>(a.logits, E, lane, lgt);
-    }
-    // the routing wave does nothing else until it has routed: the call tag and
-    // the tables come from the other waves (first used after the barrier that
-    // follows routing)
+    // call tag, activation units and the routing logits are all fetched at
+    // once: wave w < NWL loads the logits of experts 64w .. 64w + 63
+    const int NWL = (E + WAVE - 1) / WAVE;
+    float lg1 = 0.f;
+    if (wv < NWL) lg1 = a.logits[min(WAVE * wv + lane, E - 1)];
     if (tid == 64) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
     if (tid >= 128 && tid < 134) (&S.stale[0][0])[tid - 128] = 0u;
     if (wv > 0) build_luts<FMT>(Lt, tid - 64, D1_THREADS - 64, DEC == DEC_LUT);
@@ -143,15 +170,47 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
         load_x_units<QG, 1>(xr, xp, UH, lrg, LPRg);
     }
 
-    // ------------------------------------------------ route (every workgroup, wave 0)
+    // ------------------------------------------------ route (every workgroup), by ranks
+    // Every expert has a unique 64-bit key (larger key: larger logit, or the
+    // same logit and a lower index), so its rank is the number of larger keys.
+    // Level 1: wave w < NWL ranks its 64 experts among themselves (all compares
+    // in parallel, no serial rounds) and lists those of rank < k.  Level 2: the
+    // NWL * k listed keys are ranked among themselves; rank r < k is the
+    // expert of rank r overall.
+    const int KS = (k + 1) & ~1;   // list stride (even: 16-byte pair reads)
+    if (wv < NWL) {
+        const uint64_t key = expert_key(lg1, WAVE * wv + lane, WAVE * wv + lane < E);
+        S.lkey[wv][lane] = key;
+        __builtin_amdgcn_wave_barrier();   // the wave's own LDS writes precede its reads
+        const int rank = d1_count_greater<WAVE>(S.lkey[wv], key);
+        if (rank < k) S.cand[wv * KS + rank] = key;
+        if (lane == 0 && KS > k) S.cand[wv * KS + k] = 0ull;   // padding: below every key
+    }
+    __syncthreads();
+    {
+        // candidate c's global rank: the sum over the lists of how many of
+        // their keys are larger (exact for the top k: fewer than k keys of any
+        // list are larger than such a candidate, so all of them are listed);
+        // GS adjacent lanes take one candidate, one list each
+        const int nc = NWL * KS;
+        const int GS = NWL <= 1 ? 1 : NWL <= 2 ? 2 : NWL <= 4 ? 4 : NWL <= 8 ? 8 : 16;
+        for (int t0 = 0; t0 < nc * GS; t0 += D1_THREADS) {
+            const int t = t0 + tid, c = t / GS, wl = t - c * GS;
+            uint64_t key = 0;
+            int cnt = 0;
+            if (c < nc) {
+                key = S.cand[c];
+                if (wl < NWL) cnt = d1_count_greater_list(S.cand + wl * KS, KS, key);
+            }
+            for (int off = GS >> 1; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+            if (c < nc && wl == 0 && (c % KS) < k && cnt < k) S.ranked[cnt] = key;
+        }
+    }
+    __syncthreads();
     if (wv == 0) {
         int e;
         float wt;
-        if (E <= 64) route_from_logits<1>(reinterpret_cast<const float(&)[1]>(lgt), E, k, lane, e, wt);
-        else if (E <= 128) route_from_logits<2>(reinterpret_cast<const float(&)[2]>(lgt), E, k, lane, e, wt);
-        else if (E <= 256) route_from_logits<4>(reinterpret_cast<const float(&)[4]>(lgt), E, k, lane, e, wt);
-        else if (E <= 512) route_from_logits<8>(reinterpret_cast<const float(&)[8]>(lgt), E, k, lane, e, wt);
-        else route_from_logits<16>(lgt, E, k, lane, e, wt);
+        weights_from_ranked(lane < k ? S.ranked[lane] : 0ull, k, lane, e, wt);
         if (lane < k) {
             S.sel[lane] = e;
             S.wsel[lane] = wt;
@@ -471,7 +530,8 @@ hipError_t decode1_fd(const DecodeArgs &a, hipStream_t s) {
     if (a.T != 1 || a.mode != MODE_ROUTE) return hipErrorNotSupported;
     const int NG = L.k + (L.Ish > 0 ? 1 : 0);
     const int Imax = L.I > L.Ish ? L.I : L.Ish;
-    if (NG > D1_MAX_GROUPS || NG * Imax > D1_H_LDS_WORDS || NG * Imax / 2 > D1_NB0 * D1_THREADS)
+    if (NG > D1_MAX_GROUPS || NG * Imax > D1_H_LDS_WORDS || NG * Imax / 2 > D1_NB0 * D1_THREADS ||
+        L.E > WAVE * D1_MAX_LISTS)
         return hipErrorNotSupported;
     const int UH = L.H / 32, LPRg = lanes_per_row(UH), QG = (UH + LPRg - 1) / LPRg;
     const int LPRd = down_lanes_per_row(L.I, L.Ish), QD = (Imax / 32 + LPRd - 1) / LPRd;

@@ -226,3 +226,23 @@ def test_single_token_kernel_shapes(cfg):
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert max_rel_err(one.cpu().numpy(), ref) <= PARITY_TOL
     assert torch.equal(one[0], two[0])
+
+
+def test_single_token_routing_ties():
+    """The one-token kernel routes by ranks of unique keys: logits on a coarse
+    grid (many exact ties, and a tie across the k-th place) must still give the
+    oracle's picks, ties to the lower index."""
+    require_gpu()
+    cfg = SMALL
+    L = _layer(cfg)
+    for sub in range(4):
+        x, l = _inputs(cfg, 1, sub=30 + sub)
+        l = (np.round(l * 2.0) / 2.0).astype(np.float32)
+        xd, ld = dev_bf16(x), torch.from_numpy(l).cuda()
+        idx = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, cfg.top_k), dtype=torch.float32, device="cuda")
+        out = moeq.moe_layer_decode(L, xd, ld, idx_out=idx, w_out=w, flags=F32)
+        ridx, rw, ref = oracle_layer(cfg, x, l)
+        assert np.array_equal(idx.cpu().numpy(), ridx), sub
+        assert np.allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
+        assert max_rel_err(out.cpu().numpy(), ref) <= PARITY_TOL
