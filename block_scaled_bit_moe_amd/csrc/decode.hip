@@ -14,16 +14,25 @@ hipError_t decode1_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
 hipError_t decode1_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
 hipError_t decode1_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
 hipError_t decode1_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
+hipError_t decodeT_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
+hipError_t decodeT_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
+hipError_t decodeT_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
+hipError_t decodeT_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
 
-// MOEQ_DECODE1=0 routes single-token calls to the general kernel (for A/B
-// measurement; both give identical results).
+// MOEQ_DECODE1=0 routes single-token calls, MOEQ_DECODET=0 routed calls of
+// 2..16 tokens, to the general kernel (for A/B measurement; all give
+// identical results).
+static bool env_on(const char *name) {
+    const char *v = getenv(name);
+    return !(v && v[0] == '0');
+}
 static bool single_token_kernel_enabled() {
-    static int on = -1;
-    if (on < 0) {
-        const char *v = getenv("MOEQ_DECODE1");
-        on = (v && v[0] == '0') ? 0 : 1;
-    }
-    return on == 1;
+    static const bool on = env_on("MOEQ_DECODE1");
+    return on;
+}
+static bool few_token_kernel_enabled() {
+    static const bool on = env_on("MOEQ_DECODET");
+    return on;
 }
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
@@ -31,8 +40,9 @@ size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
     (void)k;
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     // header | h words of the general kernel | its fp32 partials | tagged h words of the single-token kernel
+    // | tagged h words and partial outputs of the few-token kernel
     return WS_HEADER + (size_t)DEC_MAX_PAIRS * Imax * sizeof(uint32_t) + (size_t)DEC_MAX_PAIRS * H * sizeof(float) +
-           (size_t)33 * Imax * sizeof(uint64_t);
+           (size_t)33 * Imax * sizeof(uint64_t) + (size_t)DEC_MAX_PAIRS * (Imax + H) * sizeof(uint64_t);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {
@@ -40,6 +50,13 @@ hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {
         hipError_t e;
         if (a.L.fmt == 1) e = dec == DEC_HW ? decode1_launch_e2m1_hw(a, s) : decode1_launch_e2m1_lut(a, s);
         else e = dec == DEC_HW ? decode1_launch_e2m3_hw(a, s) : decode1_launch_e2m3_lut(a, s);
+        if (e != hipErrorNotSupported) return e;
+        (void)hipGetLastError();
+    }
+    if (a.T >= 2 && a.T <= DEC_MAX_T && a.mode == MODE_ROUTE && few_token_kernel_enabled()) {
+        hipError_t e;
+        if (a.L.fmt == 1) e = dec == DEC_HW ? decodeT_launch_e2m1_hw(a, s) : decodeT_launch_e2m1_lut(a, s);
+        else e = dec == DEC_HW ? decodeT_launch_e2m3_hw(a, s) : decodeT_launch_e2m3_lut(a, s);
         if (e != hipErrorNotSupported) return e;
         (void)hipGetLastError();
     }

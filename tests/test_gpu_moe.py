@@ -167,6 +167,7 @@ def test_bounded_wait_expiry_is_reported_then_recovers():
     assert ei.value.code == moeq.MOE_EKERNEL
     assert moeq.moe_workspace_status(ws) == moeq.MOE_OK            # the read cleared it
     hdr = ws[:16384].view(torch.int32).cpu().numpy()
+    hdr[3] = 0                                                    # the call counter keeps counting
     assert not hdr.any()                                          # counters back at zero
     out = moeq.moe_layer_decode(L, xd, ld, flags=F32, ws=ws).cpu().numpy()
     _, _, ref = oracle_layer(cfg, x, l)
