@@ -41,6 +41,11 @@ constexpr size_t DT_LDS = 112 * 1024;            // dynamic LDS: one batch's x (
 constexpr int DT_MAX_GROUPS = DEC_MAX_T * 32 + 1;
 constexpr int DT_HPT = 8;                         // h pieces per thread per read pass (phase C)
 
+// Rows per lane group and pass (gate/up: row pairs), so that every lane has
+// several unit loads in flight in each of the two pipeline stages.
+__host__ __device__ constexpr int dt_rows_gu(int QG) { return QG >= 2 ? 1 : 2; }
+__host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 2 : 4; }
+
 struct DTPlan {
     int G;       // workgroups
     int rw;      // output rows per workgroup (phase D)
@@ -61,6 +66,7 @@ struct DTShared {
     int scan[2 * DT_NW];
     int n_groups, n_routed_groups;
     u32 tag;
+    int next[2];                          // work counters of even / odd batches
 };
 
 // Workspace regions of this kernel (after those of the other decode kernels):
@@ -72,6 +78,18 @@ __host__ __device__ inline size_t dt_h_offset(int H, int I, int Ish) {
 __host__ __device__ inline size_t dt_y_offset(int H, int I, int Ish) {
     const size_t Imax = (size_t)(I > Ish ? I : Ish);
     return dt_h_offset(H, I, Ish) + (size_t)DEC_MAX_PAIRS * Imax * 8;
+}
+
+// A tagged word (tag << 32 | fp32 bits) at byte offset voff + soff, written
+// with one 64-bit store through to the device coherence point (sc1), as the
+// single-token kernel's h words are.  The uniform part of the offset goes in
+// the instruction's scalar offset.
+__device__ inline void dt_store_tagged(__amdgpu_buffer_rsrc_t r, u32 voff, u32 soff, u32 tag, float v) {
+    typedef __attribute__((ext_vector_type(2))) u32 v2u;
+    v2u d;
+    d.x = __builtin_bit_cast(u32, v);
+    d.y = tag;
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voff, (int)soff, 16);
 }
 
 // exclusive scan of two counters over the 1024 threads
@@ -128,7 +146,11 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
     typedef __attribute__((ext_vector_type(4))) u32 v4u;
 
     // ------------------------------------------------ A. route, expert groups
-    if (tid == 0) S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
+    if (tid == 0) {
+        S.tag = d1_ld_relaxed(&hdr[WS_EPOCH]) + 1u;
+        S.next[0] = 0;
+        S.next[1] = 0;
+    }
     build_luts<FMT>(Lt, tid, DT_THREADS, DEC == DEC_LUT);
     for (int e = tid; e < 1024; e += DT_THREADS) S.tmask[e] = 0u;
     if (wv < T) {
@@ -189,12 +211,28 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
     __syncthreads();
     const int NG = S.n_groups, NRG = S.n_routed_groups;
     const u32 tag = S.tag;
+    // Work inside a batch (one group's row range and up to DT_XT of its tokens)
+    // is dealt to the waves one item at a time from an LDS counter, so that a
+    // wave that gets its loads served sooner takes more items and all waves
+    // finish together.  Batches alternate between two counters: batch n+1's is
+    // cleared after the barrier that opens batch n, when no wave can still
+    // take from it (its last use was batch n-1).
+    int nbatch = 0;
+    auto open_batch = [&]() {
+        if (tid == 0) S.next[(nbatch + 1) & 1] = 0;
+    };
+    auto grab = [&]() -> int {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&S.next[nbatch & 1], 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
 
     // ------------------------------------------------ B. gate | up, h published
     {
         const int UH = H / 32, LPRg = lanes_per_row(UH), RPWg = WAVE / LPRg;
         const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
         const int USx = dt_unit_stride(16, plan.xt_gu);
+        const __amdgpu_buffer_rsrc_t hw = rsrc_of(hq, (uint64_t)DEC_MAX_PAIRS * Imax * 8);
         const int UB = NRG * I + (Ish > 0 ? Ish : 0);
         const int ub1 = (int)((int64_t)UB * (w + 1) / G);
         for (int u0 = (int)((int64_t)UB * w / G); u0 < ub1;) {
@@ -203,85 +241,99 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
             const int e = S.g_expert[g], m = S.g_count[g], pos0 = S.g_start[g];
             const uint8_t *c13 = (e >= 0) ? ly.w13c + (int64_t)max(e, 0) * 2 * I * crbH : ly.sh13c;
             const uint8_t *s13 = (e >= 0) ? ly.w13s + (int64_t)max(e, 0) * 2 * I * srbH : ly.sh13s;
-            const int npass = (nsub + DT_NW * RPWg - 1) / (DT_NW * RPWg);
+            constexpr int RG = dt_rows_gu(QG);
+            const int nitem = (nsub + RG * RPWg - 1) / (RG * RPWg);
+            // row pair b of item it for this lane group
+            auto jrow = [&](int it, int b) { return (it * RG + b) * RPWg + rsg; };
             for (int tb = 0; tb < m; tb += plan.xt_gu) {
                 const int mb = min(plan.xt_gu, m - tb);
-                __syncthreads();   // the previous batch is done with s_buf
+                __syncthreads();   // the previous batch is done with s_buf and its counter
+                open_batch();
                 for (int q = tid; q < mb * UH * 4; q += DT_THREADS) {
                     const int t = q / (UH * 4), rem = q - t * (UH * 4), u = rem >> 2, v = rem & 3;
                     const uint4 val = *reinterpret_cast<const uint4 *>(a.x + (int64_t)S.p_tok[pos0 + tb + t] * H + 32 * u + 8 * v);
                     *reinterpret_cast<uint4 *>(s_buf + u * USx + 16 * t + 4 * v) = val;
                 }
                 __syncthreads();
-                // pass p: this lane group's row pair j = (wave + 16 p) * RPWg + group
-                Unit<FMT> un[2][2][QG];
+                Unit<FMT> un[2][RG][2][QG];
                 auto issue = [&](int st, int p) {
-                    const int j = (wv + DT_NW * p) * RPWg + rsg;
-                    const int r = i0 + (j < nsub ? j : 0);   // past the end: re-load the first row
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int row = h ? Ig + r : r;
-                        const uint8_t *c = c13 + (int64_t)row * crbH, *sc = s13 + (int64_t)row * srbH;
+                    for (int b = 0; b < RG; ++b) {
+                        const int j = jrow(p, b);
+                        const int r = i0 + (j < nsub ? j : 0);   // past the end: re-load the first row
 #pragma unroll
-                        for (int q = 0; q < QG; ++q) {
-                            const int u = lrg + LPRg * q;
-                            load_unit<FMT>(un[st][h][q], c, sc, u < UH ? u : lrg);
+                        for (int h = 0; h < 2; ++h) {
+                            const int row = h ? Ig + r : r;
+                            const uint8_t *c = c13 + (int64_t)row * crbH, *sc = s13 + (int64_t)row * srbH;
+#pragma unroll
+                            for (int q = 0; q < QG; ++q) {
+                                const int u = lrg + LPRg * q;
+                                load_unit<FMT>(un[st][b][h][q], c, sc, u < UH ? u : lrg);
+                            }
                         }
                     }
                 };
                 auto compute = [&](int st, int p) {
-                    float acc[2][DT_XT];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int b = 0; b < RG; ++b) {
+                        float acc[2][DT_XT];
 #pragma unroll
-                        for (int t = 0; t < DT_XT; ++t) acc[h][t] = 0.f;
+                        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                            for (int t = 0; t < DT_XT; ++t) acc[h][t] = 0.f;
 #pragma unroll
-                        for (int q = 0; q < QG; ++q) {
-                            const int u = lrg + LPRg * q;
-                            u32 wd[16];
-                            decode_unit<FMT, DEC>(un[st][h][q], Lt, wd);
-                            float s0, s1;
-                            unit_scales<FMT>(un[st][h][q], Lt, s0, s1);
-                            const int uu = u < UH ? u : 0;
-                            const uint4 *xb = reinterpret_cast<const uint4 *>(s_buf + uu * USx);
+                        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int t = 0; t < DT_XT; ++t) {
-                                if (t < mb) {
-                                    const uint4 *xt = xb + 4 * t;
-                                    u32 xv[16];
+                            for (int q = 0; q < QG; ++q) {
+                                const int u = lrg + LPRg * q;
+                                u32 wd[16];
+                                decode_unit<FMT, DEC>(un[st][b][h][q], Lt, wd);
+                                float s0, s1;
+                                unit_scales<FMT>(un[st][b][h][q], Lt, s0, s1);
+                                const int uu = u < UH ? u : 0;
+                                const uint4 *xb = reinterpret_cast<const uint4 *>(s_buf + uu * USx);
 #pragma unroll
-                                    for (int v = 0; v < 4; ++v) {
-                                        const uint4 A = xt[v];
-                                        xv[4 * v] = A.x; xv[4 * v + 1] = A.y; xv[4 * v + 2] = A.z; xv[4 * v + 3] = A.w;
+                                for (int t = 0; t < DT_XT; ++t) {
+                                    if (t < mb) {
+                                        const uint4 *xt = xb + 4 * t;
+                                        u32 xv[16];
+#pragma unroll
+                                        for (int v = 0; v < 4; ++v) {
+                                            const uint4 A = xt[v];
+                                            xv[4 * v] = A.x; xv[4 * v + 1] = A.y; xv[4 * v + 2] = A.z; xv[4 * v + 3] = A.w;
+                                        }
+                                        const float d = unit_dot<FMT>(wd, xv, s0, s1, acc[h][t]);
+                                        acc[h][t] = u < UH ? d : acc[h][t];
                                     }
-                                    const float d = unit_dot<FMT>(wd, xv, s0, s1, acc[h][t]);
-                                    acc[h][t] = u < UH ? d : acc[h][t];
                                 }
                             }
-                        }
-                    const int j = (wv + DT_NW * p) * RPWg + rsg;
+                        const int j = jrow(p, b);
 #pragma unroll
-                    for (int t = 0; t < DT_XT; ++t) {
-                        if (t < mb) {
-                            const float gsum = group_sum_dpp(acc[0][t], LPRg), usum = group_sum_dpp(acc[1][t], LPRg);
-                            if (j < nsub && lrg == 0) {
-                                const float hv = silu_f32(gsum) * usum;
-                                __hip_atomic_store(hq + (size_t)(pos0 + tb + t) * Imax + (i0 + j),
-                                                   ((uint64_t)tag << 32) | __builtin_bit_cast(u32, hv), __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        for (int t = 0; t < DT_XT; ++t) {
+                            if (t < mb) {
+                                const float gsum = group_sum_dpp(acc[0][t], LPRg), usum = group_sum_dpp(acc[1][t], LPRg);
+                                if (j < nsub && lrg == 0) {
+                                    const float hv = silu_f32(gsum) * usum;
+                                    dt_store_tagged(hw, (u32)(i0 + j) * 8u, (u32)((pos0 + tb + t) * Imax) * 8u, tag, hv);
+                                }
                             }
                         }
                     }
                 };
-                issue(0, 0);
-                for (int p = 0; p < npass; p += 2) {
-                    issue(1, p + 1);
-                    compute(0, p);
-                    issue(0, p + 2);
-                    compute(1, p + 1);
+                // two items in flight per wave; an item past the end loads the first rows again
+                int ia = grab();
+                issue(0, ia);
+                for (;;) {
+                    const int ib = grab();
+                    issue(1, ib);
+                    if (ia >= nitem) break;
+                    compute(0, ia);
+                    ia = grab();
+                    issue(0, ia);
+                    if (ib >= nitem) break;
+                    compute(1, ib);
                 }
+                ++nbatch;
             }
             u0 += nsub;
         }
@@ -296,6 +348,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         const int LPRd = down_lanes_per_row(I, Ish), RPWd = WAVE / LPRd;
         const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
         const int USh = dt_unit_stride(32, plan.xt_dn);
+        const __amdgpu_buffer_rsrc_t yw = rsrc_of(yq, (uint64_t)DEC_MAX_PAIRS * H * 8);
         const int UD = NG * H;
         const int ud1 = (int)((int64_t)UD * (w + 1) / G);
         const __amdgpu_buffer_rsrc_t hr = rsrc_of(hq, (uint64_t)DEC_MAX_PAIRS * Imax * 8);
@@ -306,22 +359,30 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
             const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
             const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)max(e, 0) * H * crbI : ly.sh2c;
             const uint8_t *s2 = (e >= 0) ? ly.w2s + (int64_t)max(e, 0) * H * srbI : ly.sh2s;
-            const int npass = (nsub + DT_NW * RPWd - 1) / (DT_NW * RPWd);
+            constexpr int RD = dt_rows_dn(QD);
+            const int nitem = (nsub + RD * RPWd - 1) / (RD * RPWd);
+            // row b of item it for this lane group
+            auto jrow = [&](int it, int b) { return (it * RD + b) * RPWd + rsd; };
             for (int tb = 0; tb < m; tb += plan.xt_dn) {
                 const int mb = min(plan.xt_dn, m - tb);
-                Unit<FMT> un[2][QD];
+                Unit<FMT> un[2][RD][QD];
                 auto issue = [&](int st, int p) {
-                    const int j = (wv + DT_NW * p) * RPWd + rsd;
-                    const int o = o0 + (j < nsub ? j : 0);
-                    const uint8_t *c = c2 + (int64_t)o * crbI, *sc = s2 + (int64_t)o * srbI;
 #pragma unroll
-                    for (int q = 0; q < QD; ++q) {
-                        const int u = lrd + LPRd * q;
-                        load_unit<FMT>(un[st][q], c, sc, u < UI ? u : lrd);
+                    for (int b = 0; b < RD; ++b) {
+                        const int j = jrow(p, b);
+                        const int o = o0 + (j < nsub ? j : 0);
+                        const uint8_t *c = c2 + (int64_t)o * crbI, *sc = s2 + (int64_t)o * srbI;
+#pragma unroll
+                        for (int q = 0; q < QD; ++q) {
+                            const int u = lrd + LPRd * q;
+                            load_unit<FMT>(un[st][b][q], c, sc, u < UI ? u : lrd);
+                        }
                     }
                 };
-                __syncthreads();   // the previous batch is done with s_buf
-                issue(0, 0);       // the weights do not depend on h: in flight during its wait
+                __syncthreads();   // the previous batch is done with s_buf and its counter
+                open_batch();
+                int ia = grab();
+                issue(0, ia);      // the weights do not depend on h: in flight during its wait
                 // h of this batch: token t's Ig/2 pieces of two tagged words, into LDS as hi/lo pairs
                 {
                     const int npc = mb * (Ig / 2);
@@ -371,51 +432,57 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                 }
                 __syncthreads();
                 auto compute = [&](int st, int p) {
-                    float acc[DT_XT];
 #pragma unroll
-                    for (int t = 0; t < DT_XT; ++t) acc[t] = 0.f;
+                    for (int b = 0; b < RD; ++b) {
+                        float acc[DT_XT];
 #pragma unroll
-                    for (int q = 0; q < QD; ++q) {
-                        const int u = lrd + LPRd * q;
-                        const int uu = u < UI ? u : 0;
-                        u32 wd[16];
-                        decode_unit<FMT, DEC>(un[st][q], Lt, wd);
-                        float s0, s1;
-                        unit_scales<FMT>(un[st][q], Lt, s0, s1);
+                        for (int t = 0; t < DT_XT; ++t) acc[t] = 0.f;
+#pragma unroll
+                        for (int q = 0; q < QD; ++q) {
+                            const int u = lrd + LPRd * q;
+                            const int uu = u < UI ? u : 0;
+                            u32 wd[16];
+                            decode_unit<FMT, DEC>(un[st][b][q], Lt, wd);
+                            float s0, s1;
+                            unit_scales<FMT>(un[st][b][q], Lt, s0, s1);
+#pragma unroll
+                            for (int t = 0; t < DT_XT; ++t) {
+                                if (t < mb) {
+                                    const uint4 *hb = reinterpret_cast<const uint4 *>(s_buf + uu * USh + 32 * t);
+                                    u32 xh[16], xl[16];
+#pragma unroll
+                                    for (int vv = 0; vv < 4; ++vv) {
+                                        const uint4 A = hb[vv], B = hb[4 + vv];
+                                        xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
+                                        xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
+                                    }
+                                    const float d = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc[t]);
+                                    acc[t] = u < UI ? d : acc[t];
+                                }
+                            }
+                        }
+                        const int j = jrow(p, b);
 #pragma unroll
                         for (int t = 0; t < DT_XT; ++t) {
                             if (t < mb) {
-                                const uint4 *hb = reinterpret_cast<const uint4 *>(s_buf + uu * USh + 32 * t);
-                                u32 xh[16], xl[16];
-#pragma unroll
-                                for (int vv = 0; vv < 4; ++vv) {
-                                    const uint4 A = hb[vv], B = hb[4 + vv];
-                                    xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
-                                    xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
-                                }
-                                const float d = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc[t]);
-                                acc[t] = u < UI ? d : acc[t];
+                                const float ysum = group_sum_dpp(acc[t], LPRd);
+                                if (j < nsub && lrd == 0)
+                                    dt_store_tagged(yw, (u32)(o0 + j) * 8u, (u32)((pos0 + tb + t) * H) * 8u, tag, ysum);
                             }
                         }
                     }
-                    const int j = (wv + DT_NW * p) * RPWd + rsd;
-#pragma unroll
-                    for (int t = 0; t < DT_XT; ++t) {
-                        if (t < mb) {
-                            const float ysum = group_sum_dpp(acc[t], LPRd);
-                            if (j < nsub && lrd == 0)
-                                __hip_atomic_store(yq + (size_t)(pos0 + tb + t) * H + (o0 + j),
-                                                   ((uint64_t)tag << 32) | __builtin_bit_cast(u32, ysum), __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                    }
                 };
-                for (int p = 0; p < npass; p += 2) {
-                    issue(1, p + 1);
-                    compute(0, p);
-                    issue(0, p + 2);
-                    compute(1, p + 1);
+                for (;;) {
+                    const int ib = grab();
+                    issue(1, ib);
+                    if (ia >= nitem) break;
+                    compute(0, ia);
+                    ia = grab();
+                    issue(0, ia);
+                    if (ib >= nitem) break;
+                    compute(1, ib);
                 }
+                ++nbatch;
             }
             u0 += nsub;
         }
