@@ -44,7 +44,30 @@ constexpr int DT_HPT = 8;                         // h pieces per thread per rea
 // Rows per lane group and pass (gate/up: row pairs), so that every lane has
 // several unit loads in flight in each of the two pipeline stages.
 __host__ __device__ constexpr int dt_rows_gu(int QG) { return QG >= 2 ? 1 : 2; }
-__host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 2 : 4; }
+__host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 1 : 2; }
+
+// Relative cost of one row (gate/up: one row pair) of a group with m tokens:
+// streaming its weights plus m dot products.  The static split of each phase
+// gives every workgroup an equal share of this cost rather than of the rows,
+// so that workgroups holding experts with several tokens get fewer rows.  The
+// constants are the ratios measured on a 6144-wide layer with 2048-wide
+// experts (e2m3 rows carry 6.25 instead of 4.5 bits per weight).
+template <int FMT> __host__ __device__ constexpr int dt_cost_gu(int m) { return (FMT == FMT_E2M1 ? 6 : 8) + 2 * m; }
+template <int FMT> __host__ __device__ constexpr int dt_cost_dn(int m) { return (FMT == FMT_E2M1 ? 3 : 4) + 2 * m; }
+
+// The first group g with cum[g + 1] > c (cum ascending, cum[0] = 0, c < cum[n]).
+__device__ inline int dt_first_group(const int *cum, int n, int c) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cum[mid + 1] > c) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+// Rows r of a group whose cost position cum + r * cost falls below c: the
+// ranges [row_at(c0), row_at(c1)) of consecutive shares partition the rows.
+__device__ inline int dt_row_at(int c, int cost) { return c <= 0 ? 0 : (c + cost - 1) / cost; }
 
 struct DTPlan {
     int G;       // workgroups
@@ -67,6 +90,8 @@ struct DTShared {
     int n_groups, n_routed_groups;
     u32 tag;
     int next[2];                          // work counters of even / odd batches
+    int cum_gu[DT_MAX_GROUPS + 1];        // cost of the groups before g (gate/up, down)
+    int cum_dn[DT_MAX_GROUPS + 1];
 };
 
 // Workspace regions of this kernel (after those of the other decode kernels):
@@ -209,7 +234,27 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         S.pos_of[t][r] = (short)(S.g_start[S.e2g[e]] + __builtin_popcount(S.tmask[e] & ((1u << t) - 1u)));
     }
     __syncthreads();
-    const int NG = S.n_groups, NRG = S.n_routed_groups;
+    {
+        const int g = tid;
+        int cgu = 0, cdn = 0;
+        if (g < S.n_groups) {
+            const int m = S.g_count[g], Ig = (S.g_expert[g] >= 0) ? I : Ish;
+            cgu = Ig * dt_cost_gu<FMT>(m);
+            cdn = H * dt_cost_dn<FMT>(m);
+        }
+        int eg, ed, tg, td;
+        dt_exscan2(cgu, cdn, eg, ed, tg, td, S.scan);
+        if (g < S.n_groups) {
+            S.cum_gu[g] = eg;
+            S.cum_dn[g] = ed;
+        }
+        if (tid == 0) {
+            S.cum_gu[S.n_groups] = tg;
+            S.cum_dn[S.n_groups] = td;
+        }
+    }
+    __syncthreads();
+    const int NG = S.n_groups;
     const u32 tag = S.tag;
     // Work inside a batch (one group's row range and up to DT_XT of its tokens)
     // is dealt to the waves one item at a time from an LDS counter, so that a
@@ -233,12 +278,13 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         const int lrg = lane & (LPRg - 1), rsg = lane / LPRg;
         const int USx = dt_unit_stride(16, plan.xt_gu);
         const __amdgpu_buffer_rsrc_t hw = rsrc_of(hq, (uint64_t)DEC_MAX_PAIRS * Imax * 8);
-        const int UB = NRG * I + (Ish > 0 ? Ish : 0);
-        const int ub1 = (int)((int64_t)UB * (w + 1) / G);
-        for (int u0 = (int)((int64_t)UB * w / G); u0 < ub1;) {
-            const int g = min(u0 / I, NRG), gbase = g * I, Ig = (g < NRG) ? I : Ish;
-            const int i0 = u0 - gbase, nsub = min(ub1, gbase + Ig) - u0;
-            const int e = S.g_expert[g], m = S.g_count[g], pos0 = S.g_start[g];
+        const int c0 = (int)((int64_t)S.cum_gu[NG] * w / G), c1 = (int)((int64_t)S.cum_gu[NG] * (w + 1) / G);
+        for (int g = dt_first_group(S.cum_gu, NG, c0); g < NG && S.cum_gu[g] < c1; ++g) {
+            const int e = S.g_expert[g], m = S.g_count[g], pos0 = S.g_start[g], Ig = (e >= 0) ? I : Ish;
+            const int cost = dt_cost_gu<FMT>(m);
+            const int i0 = dt_row_at(c0 - S.cum_gu[g], cost), i1 = min(Ig, dt_row_at(c1 - S.cum_gu[g], cost));
+            if (i0 >= i1) continue;
+            const int nsub = i1 - i0;
             const uint8_t *c13 = (e >= 0) ? ly.w13c + (int64_t)max(e, 0) * 2 * I * crbH : ly.sh13c;
             const uint8_t *s13 = (e >= 0) ? ly.w13s + (int64_t)max(e, 0) * 2 * I * srbH : ly.sh13s;
             constexpr int RG = dt_rows_gu(QG);
@@ -335,7 +381,6 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                 }
                 ++nbatch;
             }
-            u0 += nsub;
         }
     }
 
@@ -349,12 +394,14 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         const int lrd = lane & (LPRd - 1), rsd = lane / LPRd;
         const int USh = dt_unit_stride(32, plan.xt_dn);
         const __amdgpu_buffer_rsrc_t yw = rsrc_of(yq, (uint64_t)DEC_MAX_PAIRS * H * 8);
-        const int UD = NG * H;
-        const int ud1 = (int)((int64_t)UD * (w + 1) / G);
         const __amdgpu_buffer_rsrc_t hr = rsrc_of(hq, (uint64_t)DEC_MAX_PAIRS * Imax * 8);
-        for (int u0 = (int)((int64_t)UD * w / G); u0 < ud1;) {
-            const int g = u0 / H, o0 = u0 - g * H, nsub = min(ud1, (g + 1) * H) - u0;
+        const int c0 = (int)((int64_t)S.cum_dn[NG] * w / G), c1 = (int)((int64_t)S.cum_dn[NG] * (w + 1) / G);
+        for (int g = dt_first_group(S.cum_dn, NG, c0); g < NG && S.cum_dn[g] < c1; ++g) {
             const int e = S.g_expert[g], m = S.g_count[g], pos0 = S.g_start[g];
+            const int cost = dt_cost_dn<FMT>(m);
+            const int o0 = dt_row_at(c0 - S.cum_dn[g], cost), o1 = min(H, dt_row_at(c1 - S.cum_dn[g], cost));
+            if (o0 >= o1) continue;
+            const int nsub = o1 - o0;
             const int Ig = (e >= 0) ? I : Ish, UI = Ig / 32;
             const int64_t crbI = Fmt<FMT>::code_row_bytes(Ig), srbI = Fmt<FMT>::scale_row_bytes(Ig);
             const uint8_t *c2 = (e >= 0) ? ly.w2c + (int64_t)max(e, 0) * H * crbI : ly.sh2c;
@@ -431,41 +478,50 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                     }
                 }
                 __syncthreads();
-                auto compute = [&](int st, int p) {
+                auto compute = [&](int st, int it) {
+                    float acc[RD][DT_XT];
 #pragma unroll
-                    for (int b = 0; b < RD; ++b) {
-                        float acc[DT_XT];
+                    for (int b = 0; b < RD; ++b)
 #pragma unroll
-                        for (int t = 0; t < DT_XT; ++t) acc[t] = 0.f;
+                        for (int t = 0; t < DT_XT; ++t) acc[b][t] = 0.f;
 #pragma unroll
-                        for (int q = 0; q < QD; ++q) {
-                            const int u = lrd + LPRd * q;
-                            const int uu = u < UI ? u : 0;
-                            u32 wd[16];
-                            decode_unit<FMT, DEC>(un[st][b][q], Lt, wd);
-                            float s0, s1;
-                            unit_scales<FMT>(un[st][b][q], Lt, s0, s1);
+                    for (int q = 0; q < QD; ++q) {
+                        const int u = lrd + LPRd * q;
+                        const int uu = u < UI ? u : 0;
+                        // this lane's unit of each row, decoded once; each h unit read once for all rows
+                        u32 wd[RD][16];
+                        float s0[RD], s1[RD];
 #pragma unroll
-                            for (int t = 0; t < DT_XT; ++t) {
-                                if (t < mb) {
-                                    const uint4 *hb = reinterpret_cast<const uint4 *>(s_buf + uu * USh + 32 * t);
-                                    u32 xh[16], xl[16];
-#pragma unroll
-                                    for (int vv = 0; vv < 4; ++vv) {
-                                        const uint4 A = hb[vv], B = hb[4 + vv];
-                                        xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
-                                        xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
-                                    }
-                                    const float d = unit_dot_split<FMT>(wd, xh, xl, s0, s1, acc[t]);
-                                    acc[t] = u < UI ? d : acc[t];
-                                }
-                            }
+                        for (int b = 0; b < RD; ++b) {
+                            decode_unit<FMT, DEC>(un[st][b][q], Lt, wd[b]);
+                            unit_scales<FMT>(un[st][b][q], Lt, s0[b], s1[b]);
                         }
-                        const int j = jrow(p, b);
 #pragma unroll
                         for (int t = 0; t < DT_XT; ++t) {
                             if (t < mb) {
-                                const float ysum = group_sum_dpp(acc[t], LPRd);
+                                const uint4 *hb = reinterpret_cast<const uint4 *>(s_buf + uu * USh + 32 * t);
+                                u32 xh[16], xl[16];
+#pragma unroll
+                                for (int vv = 0; vv < 4; ++vv) {
+                                    const uint4 A = hb[vv], B = hb[4 + vv];
+                                    xh[4 * vv] = A.x; xh[4 * vv + 1] = A.y; xh[4 * vv + 2] = A.z; xh[4 * vv + 3] = A.w;
+                                    xl[4 * vv] = B.x; xl[4 * vv + 1] = B.y; xl[4 * vv + 2] = B.z; xl[4 * vv + 3] = B.w;
+                                }
+#pragma unroll
+                                for (int b = 0; b < RD; ++b) {
+                                    const float d = unit_dot_split<FMT>(wd[b], xh, xl, s0[b], s1[b], acc[b][t]);
+                                    acc[b][t] = u < UI ? d : acc[b][t];
+                                }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int b = 0; b < RD; ++b) {
+                        const int j = jrow(it, b);
+#pragma unroll
+                        for (int t = 0; t < DT_XT; ++t) {
+                            if (t < mb) {
+                                const float ysum = group_sum_dpp(acc[b][t], LPRd);
                                 if (j < nsub && lrd == 0)
                                     dt_store_tagged(yw, (u32)(o0 + j) * 8u, (u32)((pos0 + tb + t) * H) * 8u, tag, ysum);
                             }
@@ -484,7 +540,6 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                 }
                 ++nbatch;
             }
-            u0 += nsub;
         }
     }
 
