@@ -45,6 +45,7 @@ constexpr int DT_HPT = 8;                         // h pieces per thread per rea
 // several unit loads in flight in each of the two pipeline stages.
 __host__ __device__ constexpr int dt_rows_gu(int QG) { return QG >= 2 ? 1 : 2; }
 __host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 1 : 2; }
+constexpr int DT_STAGES_DN = 2;   // items in flight per wave on the down side (2 or 3)
 
 // Relative cost of one row (gate/up: one row pair) of a group with m tokens:
 // streaming its weights plus m dot products.  The static split of each phase
@@ -205,11 +206,16 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         const u32 m = (e < E) ? S.tmask[e] : 0u;
         int ef, ec, nf, nc;
         dt_exscan2(m != 0u, __builtin_popcount(m), ef, ec, nf, nc, S.scan);
+        // the costs are affine in m, so their prefix over the routed groups follows from the same scan
+        constexpr int gu0 = dt_cost_gu<FMT>(0), gu1 = dt_cost_gu<FMT>(1) - gu0;
+        constexpr int dn0 = dt_cost_dn<FMT>(0), dn1 = dt_cost_dn<FMT>(1) - dn0;
         if (m != 0u) {
             S.e2g[e] = (short)ef;
             S.g_expert[ef] = (short)e;
             S.g_start[ef] = (short)ec;
             S.g_count[ef] = (unsigned char)__builtin_popcount(m);
+            S.cum_gu[ef] = I * (gu0 * ef + gu1 * ec);
+            S.cum_dn[ef] = H * (dn0 * ef + dn1 * ec);
             u32 mm = m;
             for (int n = 0; mm; ++n) {
                 S.p_tok[ec + n] = (unsigned char)__builtin_ctz(mm);
@@ -219,41 +225,28 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
         if (tid == 0) {
             S.n_routed_groups = nf;
             S.n_groups = nf + (Ish > 0 ? 1 : 0);
+            int cg = I * (gu0 * nf + gu1 * nc), cd = H * (dn0 * nf + dn1 * nc);
             if (Ish > 0) {
                 S.g_expert[nf] = -1;
                 S.g_start[nf] = (short)nc;
                 S.g_count[nf] = (unsigned char)T;
+                S.cum_gu[nf] = cg;
+                S.cum_dn[nf] = cd;
+                cg += Ish * dt_cost_gu<FMT>(T);
+                cd += H * dt_cost_dn<FMT>(T);
             }
+            S.cum_gu[S.n_groups] = cg;
+            S.cum_dn[S.n_groups] = cd;
         }
         if (Ish > 0 && tid < T) S.p_tok[nc + tid] = (unsigned char)tid;
         if (Ish > 0 && tid < T) S.pos_of[tid][k] = (short)(nc + tid);
     }
     __syncthreads();
+    // pair position of every (token, rank); read only by the combine, after a later barrier
     for (int p = tid; p < T * k; p += DT_THREADS) {
         const int t = p / k, r = p - t * k, e = S.idx[p];
         S.pos_of[t][r] = (short)(S.g_start[S.e2g[e]] + __builtin_popcount(S.tmask[e] & ((1u << t) - 1u)));
     }
-    __syncthreads();
-    {
-        const int g = tid;
-        int cgu = 0, cdn = 0;
-        if (g < S.n_groups) {
-            const int m = S.g_count[g], Ig = (S.g_expert[g] >= 0) ? I : Ish;
-            cgu = Ig * dt_cost_gu<FMT>(m);
-            cdn = H * dt_cost_dn<FMT>(m);
-        }
-        int eg, ed, tg, td;
-        dt_exscan2(cgu, cdn, eg, ed, tg, td, S.scan);
-        if (g < S.n_groups) {
-            S.cum_gu[g] = eg;
-            S.cum_dn[g] = ed;
-        }
-        if (tid == 0) {
-            S.cum_gu[S.n_groups] = tg;
-            S.cum_dn[S.n_groups] = td;
-        }
-    }
-    __syncthreads();
     const int NG = S.n_groups;
     const u32 tag = S.tag;
     // Work inside a batch (one group's row range and up to DT_XT of its tokens)
@@ -412,7 +405,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
             auto jrow = [&](int it, int b) { return (it * RD + b) * RPWd + rsd; };
             for (int tb = 0; tb < m; tb += plan.xt_dn) {
                 const int mb = min(plan.xt_dn, m - tb);
-                Unit<FMT> un[2][RD][QD];
+                Unit<FMT> un[DT_STAGES_DN][RD][QD];
                 auto issue = [&](int st, int p) {
 #pragma unroll
                     for (int b = 0; b < RD; ++b) {
@@ -528,15 +521,34 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                         }
                     }
                 };
-                for (;;) {
-                    const int ib = grab();
+                if constexpr (DT_STAGES_DN == 2) {
+                    for (;;) {
+                        const int ib = grab();
+                        issue(1, ib);
+                        if (ia >= nitem) break;
+                        compute(0, ia);
+                        ia = grab();
+                        issue(0, ia);
+                        if (ib >= nitem) break;
+                        compute(1, ib);
+                    }
+                } else {
+                    int ib = grab();
                     issue(1, ib);
-                    if (ia >= nitem) break;
-                    compute(0, ia);
-                    ia = grab();
-                    issue(0, ia);
-                    if (ib >= nitem) break;
-                    compute(1, ib);
+                    for (;;) {
+                        const int ic = grab();
+                        issue(2, ic);
+                        if (ia >= nitem) break;
+                        compute(0, ia);
+                        ia = grab();
+                        issue(0, ia);
+                        if (ib >= nitem) break;
+                        compute(1, ib);
+                        ib = grab();
+                        issue(1, ib);
+                        if (ic >= nitem) break;
+                        compute(2, ic);
+                    }
                 }
                 ++nbatch;
             }
@@ -544,6 +556,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
     }
 
     // ------------------------------------------------ D. combine rows [w*RW, (w+1)*RW) of every token
+    __syncthreads();
     {
         const int oo0 = w * plan.rw, nro = max(0, min(H, oo0 + plan.rw) - oo0);
         const int kk = k + (Ish > 0 ? 1 : 0);
