@@ -4,133 +4,22 @@
 // "Decode round 2": aligned 16-byte weight loads, codebook lookups kept off the
 // critical path).
 //
-// Bandwidth-bound: every weight byte is read from HBM once per pass of MT
-// tokens.  For several tokens each workgroup streams a contiguous range of row
-// chunks through an LDS ring (stream.h): the x registers of 4 tokens leave no
-// room for deep register pipelines.  One workgroup per CU (the ring takes most
-// of the LDS), chunks split evenly over the workgroups.  For one token the
-// register-pipelined kernel below is faster (measured: 25.5 vs 39.6 us on the
-// 25600 x 5120 e2m3 matrix).
+// Bandwidth-bound: every weight byte is read from HBM once per pass of up to
+// eight tokens.  One token: x stays in registers and each wave streams its
+// row groups (register pipeline, two workgroups per CU).  Several tokens: their
+// x does not fit in registers, so one 16-wave workgroup per CU holds it in LDS
+// and deals its row range to the waves (measured on the 25600 x 5120 e2m3
+// matrix: B=4 in 35 us against 59 us for a 4-wave LDS-ring design; B=1 in 23
+// us with the register pipeline against 24 us with the 16-wave kernel).
 #include "kernels.h"
 #include "rowdot.h"
-#include "stream.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moeq {
 
-constexpr int GEMV_L = 7;    // 16-byte loads per thread per chunk: 28 KiB stages
-constexpr int GEMV_NS = 4;   // stages in flight
 constexpr int GEMV_REG_WG_PER_CU = 2;   // one-token kernel: workgroups per CU (its occupancy)
-
-template <int FMT, int DEC, int Q, int MT>
-__global__ __launch_bounds__(256) void gemv_ring_kernel(const uint8_t *__restrict__ codes,
-                                                   const uint8_t *__restrict__ scales, int rows, int cols,
-                                                   const uint16_t *__restrict__ x, int B, void *__restrict__ y,
-                                                   int out_f32, int RC, int cpw) {
-    constexpr int L_ = GEMV_L, STAGE = L_ * 4096;
-    static_assert(GEMV_NS == 4, "four stage objects");
-    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
-    // four stages as separate objects: the compiler can then tell a copy into
-    // one stage from reads of another and does not drain the pipeline
-    __shared__ __attribute__((aligned(1024))) uint8_t ring0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring2[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring3[STAGE];
-    __shared__ u32 s_pair[PAIR];
-    __shared__ float s_scale[LUT_SCALE];
-    const Luts Lt{s_pair, s_scale};
-    const int tid = threadIdx.x;
-    build_luts<FMT>(Lt, tid, 256, DEC == DEC_LUT);
-    __syncthreads();
-
-    const int crb = (int)Fmt<FMT>::code_row_bytes(cols), srb = (int)Fmt<FMT>::scale_row_bytes(cols);
-    const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
-    const int lane = tid & 63, w = tid >> 6, lr = lane & (LPR - 1), rsub = lane / LPR;
-    const __amdgpu_buffer_rsrc_t rc = rsrc_of(codes, (uint64_t)rows * crb);
-    const __amdgpu_buffer_rsrc_t rs = rsrc_of(scales, (uint64_t)rows * srb);
-    const int NC = (rows + RC - 1) / RC;
-    const int c0 = blockIdx.x * cpw;
-    const int n = (c0 + cpw < NC ? c0 + cpw : NC) - c0;
-    if (n <= 0) return;   // uniform over the workgroup
-
-    auto stage = [&](auto sc) -> uint8_t * {
-        constexpr int S = decltype(sc)::value;
-        if constexpr (S == 0) return ring0;
-        else if constexpr (S == 1) return ring1;
-        else if constexpr (S == 2) return ring2;
-        else return ring3;
-    };
-    auto src = [&](int i) {
-        const int r0 = (c0 + i) * RC;
-        const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
-        return chunk_src(rc, rs, r0, nr, (u32)crb, (u32)srb);
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-
-    for (int t0 = 0; t0 < B; t0 += MT) {
-        u32 xr[Q][MT][16];
-        const uint16_t *xp[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) xp[t] = (t0 + t < B) ? x + (int64_t)(t0 + t) * cols : nullptr;
-        load_x_units<Q, MT>(xr, xp, U, lr, LPR);
-        wait_vm<0>();   // x in registers before the ring starts
-
-        // chunks 0..2 in flight; chunk i lives in stage i % 4
-        issue_chunk<L_>(stage(I0{}), src(0), tid);
-        if (1 < n) issue_chunk<L_>(stage(I1{}), src(1), tid);
-        if (2 < n) issue_chunk<L_>(stage(I2{}), src(2), tid);
-
-        // Chunk i: wait for this thread's loads of it (loads retire in issue
-        // order; chunks i+1, i+2 may still be in flight), barrier (every
-        // thread's loads landed, and every wave finished chunk i-1, whose
-        // stage the copy of chunk i+3 then reuses), compute.
-        auto step = [&](auto dc, int i) {
-            constexpr int d = decltype(dc)::value;
-            if (i + 2 < n) wait_vm<2 * L_>();
-            else if (i + 1 < n) wait_vm<L_>();
-            else wait_vm<0>();
-            ring_barrier();
-            if (i + 3 < n) issue_chunk<L_>(stage(std::integral_constant<int, (d + 3) % 4>{}), src(i + 3), tid);
-            const int r0 = (c0 + i) * RC;
-            const int nr = (r0 + RC < rows ? r0 + RC : rows) - r0;
-            const uint8_t *sc = stage(dc);
-            const uint8_t *ss = sc + ((nr * crb + 1023) / 1024) * 1024 + ((r0 * srb) & 15);
-            constexpr int R = 2;
-            for (int base = w * RPW; base < nr; base += RING_WAVES * RPW * R) {
-                int row[R];
-#pragma unroll
-                for (int b = 0; b < R; ++b) {
-                    const int rr = base + b * RING_WAVES * RPW + rsub;
-                    row[b] = rr < nr ? rr : -1;
-                }
-                float acc[R][MT];
-                rows_dot_lds<FMT, DEC, Q, MT, R, false>(sc, ss, row, crb, srb, U, lr, LPR, xr, xr, Lt, acc);
-#pragma unroll
-                for (int b = 0; b < R; ++b) {
-                    if (row[b] < 0 || lr != 0) continue;
-#pragma unroll
-                    for (int t = 0; t < MT; ++t) {
-                        if (t0 + t >= B) continue;
-                        const int64_t o = (int64_t)(t0 + t) * rows + r0 + row[b];
-                        if (out_f32) reinterpret_cast<float *>(y)[o] = acc[b][t];
-                        else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(acc[b][t]);
-                    }
-                }
-            }
-        };
-        for (int i = 0; i < n; i += 4) {
-            step(I0{}, i);
-            if (i + 1 < n) step(I1{}, i + 1);
-            if (i + 2 < n) step(I2{}, i + 2);
-            if (i + 3 < n) step(I3{}, i + 3);
-        }
-        ring_barrier();   // every wave is done with the ring before the next token pass refills it
-    }
-}
 
 static int num_cus() {
     static int cus = 0;
@@ -143,25 +32,10 @@ static int num_cus() {
     return cus;
 }
 
-template <int FMT, int DEC, int Q, int MT>
-static hipError_t gemv_ring_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
-                          void *y, int out_f32, hipStream_t s) {
-    const int crb = (int)Fmt<FMT>::code_row_bytes(cols), srb = (int)Fmt<FMT>::scale_row_bytes(cols);
-    const int RC = rows_per_chunk(GEMV_L, crb, srb);
-    const int NC = (rows + RC - 1) / RC;
-    const int G0 = num_cus();
-    const int cpw = (NC + G0 - 1) / G0;
-    const int G = (NC + cpw - 1) / cpw;
-    hipLaunchKernelGGL((gemv_ring_kernel<FMT, DEC, Q, MT>), dim3(G), dim3(256), 0, s, codes, scales, rows, cols, x, B, y,
-                       out_f32, RC, cpw);
-    return hipGetLastError();
-}
-
 // Register-streamed variant: the x units stay in VGPRs, and each wave walks
 // its rows (every nw-th row group) R per pass with the next pass's loads in
 // flight (RowPipe).  A grid of a few workgroups per CU, so every wave streams
-// many rows after loading x once.  Used for one token, where it streams
-// faster than the ring (fewer VGPRs for x, more waves per CU).
+// many rows after loading x once.  Used for one token.
 template <int FMT, int DEC, int Q, int MT, int R>
 __global__ __launch_bounds__(256) void gemv_reg_kernel(const uint8_t *__restrict__ codes,
                                                    const uint8_t *__restrict__ scales, int rows, int cols,
@@ -232,6 +106,161 @@ static hipError_t gemv_reg_go(const uint8_t *codes, const uint8_t *scales, int r
     return hipGetLastError();
 }
 
+// 16-wave variant: one workgroup per CU streams a contiguous range of rows;
+// the tokens of a pass sit in LDS, unit-major (unit u of token t at word
+// u * (16 * xt + 4) + 16 t: the 4-word pad puts 16 consecutive units on 16
+// different bank groups, and a lane reads every token of its unit at
+// immediate offsets from one address).  Rows are dealt to the waves R at a
+// time from an LDS counter, with two items in flight per wave, so waves whose
+// loads are served sooner take more rows and all finish together.  The
+// arithmetic of a row is the register-streamed kernel's (same lanes, units,
+// order and reduction), so every token's result is the same for any batch.
+constexpr int GL_NW = 16, GL_THREADS = 64 * GL_NW, GL_XT = 8;
+constexpr size_t GL_LDS = 100 * 1024;
+
+template <int FMT, int DEC, int Q, int R>
+__global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__restrict__ codes,
+                                                        const uint8_t *__restrict__ scales, int rows, int cols,
+                                                        const uint16_t *__restrict__ x, int B, void *__restrict__ y,
+                                                        int out_f32, int xt) {
+    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
+    __shared__ u32 s_pair[PAIR];
+    __shared__ float s_scale[LUT_SCALE];
+    __shared__ int s_next[2];
+    extern __shared__ __attribute__((aligned(16))) u32 s_x[];
+    const Luts L{s_pair, s_scale};
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid == 0) {
+        s_next[0] = 0;
+        s_next[1] = 0;
+    }
+    build_luts<FMT>(L, tid, GL_THREADS, DEC == DEC_LUT);
+
+    const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
+    const int lr = lane & (LPR - 1), rs = lane / LPR;
+    const int64_t crb = Fmt<FMT>::code_row_bytes(cols), srb = Fmt<FMT>::scale_row_bytes(cols);
+    const int US = 16 * xt + 4;
+    const int r0 = (int)((int64_t)rows * blockIdx.x / gridDim.x);
+    const int nrow = (int)((int64_t)rows * (blockIdx.x + 1) / gridDim.x) - r0;
+    const int nitem = (nrow + R * RPW - 1) / (R * RPW);
+    // row b of item it for this lane group (past the range: the first row, result dropped)
+    auto jrow = [&](int it, int b) { return (it * R + b) * RPW + rs; };
+
+    int nb = 0;
+    for (int t0 = 0; t0 < B; t0 += xt) {
+        const int mb = min(xt, B - t0);
+        auto grab = [&]() -> int {
+            int v = 0;
+            if (lane == 0) v = atomicAdd(&s_next[nb & 1], 1);
+            return __builtin_amdgcn_readfirstlane(v);
+        };
+        Unit<FMT> un[2][R][Q];
+        auto issue = [&](int st, int it) {
+#pragma unroll
+            for (int b = 0; b < R; ++b) {
+                const int j = jrow(it, b);
+                const int64_t r = r0 + (j < nrow ? j : 0);
+                const uint8_t *c = codes + r * crb, *sc = scales + r * srb;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int u = lr + LPR * q;
+                    load_unit<FMT>(un[st][b][q], c, sc, u < U ? u : lr);
+                }
+            }
+        };
+        auto compute = [&](int st, int it) {
+#pragma unroll
+            for (int b = 0; b < R; ++b) {
+                float acc[GL_XT];
+#pragma unroll
+                for (int t = 0; t < GL_XT; ++t) acc[t] = 0.f;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int u = lr + LPR * q;
+                    u32 wd[16];
+                    decode_unit<FMT, DEC>(un[st][b][q], L, wd);
+                    float s0, s1;
+                    unit_scales<FMT>(un[st][b][q], L, s0, s1);
+                    const uint4 *xb = reinterpret_cast<const uint4 *>(s_x + (u < U ? u : 0) * US);
+#pragma unroll
+                    for (int t = 0; t < GL_XT; ++t) {
+                        if (t < mb) {
+                            u32 xv[16];
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const uint4 A = xb[4 * t + v];
+                                xv[4 * v] = A.x; xv[4 * v + 1] = A.y; xv[4 * v + 2] = A.z; xv[4 * v + 3] = A.w;
+                            }
+                            const float d = unit_dot<FMT>(wd, xv, s0, s1, acc[t]);
+                            acc[t] = u < U ? d : acc[t];
+                        }
+                    }
+                }
+                const int j = jrow(it, b);
+#pragma unroll
+                for (int t = 0; t < GL_XT; ++t) {
+                    if (t < mb) {
+                        const float v = group_sum_dpp(acc[t], LPR);
+                        if (j < nrow && lr == 0) {
+                            const int64_t o = (int64_t)(t0 + t) * rows + r0 + j;
+                            if (out_f32) reinterpret_cast<float *>(y)[o] = v;
+                            else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(v);
+                        }
+                    }
+                }
+            }
+        };
+        // Pass over tokens t0 .. t0+mb-1.  Its counter was cleared at the start of the
+        // previous pass (or kernel); the other one is cleared now, after the barrier
+        // that every wave passes only once done with it.
+        __syncthreads();
+        if (tid == 0) s_next[(nb + 1) & 1] = 0;
+        int ia = grab();
+        issue(0, ia);   // the weights do not depend on x: in flight while x is staged
+        for (int q = tid; q < mb * U * 4; q += GL_THREADS) {
+            const int t = q / (U * 4), rem = q - t * (U * 4), u = rem >> 2, v = rem & 3;
+            const uint4 val = *reinterpret_cast<const uint4 *>(x + (int64_t)(t0 + t) * cols + 32 * u + 8 * v);
+            *reinterpret_cast<uint4 *>(s_x + u * US + 16 * t + 4 * v) = val;
+        }
+        __syncthreads();
+        for (;;) {
+            const int ib = grab();
+            issue(1, ib);
+            if (ia >= nitem) break;
+            compute(0, ia);
+            ia = grab();
+            issue(0, ia);
+            if (ib >= nitem) break;
+            compute(1, ib);
+        }
+        ++nb;
+    }
+}
+
+template <int FMT, int DEC, int Q>
+static hipError_t gemv_lds_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
+                              void *y, int out_f32, hipStream_t s) {
+    constexpr int R = (Q >= 2) ? 1 : 2;
+    auto kern = gemv_lds_kernel<FMT, DEC, Q, R>;
+    const int U = cols / 32;
+    int xt = std::min(B, GL_XT);
+    while (xt > 1 && (size_t)U * (16 * xt + 4) * 4 > GL_LDS) --xt;
+    const size_t dyn = (size_t)U * (16 * xt + 4) * 4;
+    static size_t dyn_set = 0;   // per instantiation: dynamic LDS beyond the default limit
+    if (dyn > dyn_set) {
+        const hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+        dyn_set = dyn;
+    }
+    const int RPW = WAVE / lanes_per_row(U);
+    // one workgroup per CU, at least a few rows per wave
+    const int G = std::max(1, std::min(num_cus(), rows / (4 * GL_NW * RPW)));
+    hipLaunchKernelGGL(kern, dim3(G), dim3(GL_THREADS), dyn, s, codes, scales, rows, cols, x, B, y, out_f32, xt);
+    return hipGetLastError();
+}
+
 template <int FMT, int DEC>
 static hipError_t gemv_q(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
                          void *y, int out_f32, hipStream_t s) {
@@ -240,7 +269,7 @@ static hipError_t gemv_q(const uint8_t *codes, const uint8_t *scales, int rows, 
 #define GO(QQ)                                                                                    \
     if (Q == QQ) {                                                                                \
         if (one) return gemv_reg_go<FMT, DEC, QQ, 1>(codes, scales, rows, cols, x, B, y, out_f32, s); \
-        return gemv_ring_go<FMT, DEC, QQ, 4>(codes, scales, rows, cols, x, B, y, out_f32, s);         \
+        return gemv_lds_go<FMT, DEC, QQ>(codes, scales, rows, cols, x, B, y, out_f32, s);             \
     }
     GO(1) GO(2) GO(3) GO(4)
 #undef GO
