@@ -45,9 +45,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 def kernel_of(workload, batch=1):
     """The dominant kernel of a workload (the one the roofline is quoted for)."""
     if workload == "dense_gemv_e2m3":
-        return "gemv_reg_kernel" if batch == 1 else "gemv_ring_kernel"
+        return "gemv_reg_kernel" if batch == 1 else "gemv_lds_kernel"
     return {"wide_decode": "decode1_kernel", "toy_decode": "decode1_kernel",
-            "batched_decode": "decode_kernel", "prefill": "layer_step"}.get(workload, "kernel")
+            "batched_decode": "decodeT_kernel", "prefill": "layer_step"}.get(workload, "kernel")
 
 
 def parse():
