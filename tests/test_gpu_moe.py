@@ -247,3 +247,42 @@ def test_single_token_routing_ties():
         assert np.array_equal(idx.cpu().numpy(), ridx), sub
         assert np.allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
         assert max_rel_err(out.cpu().numpy(), ref) <= PARITY_TOL
+
+
+FEW_TOKEN_SHAPES = [
+    # H = 8192: four activation units per lane, at most six tokens of x in LDS per batch
+    MoEConfig("few_h8192", tokens=7, hidden=8192, experts=16, top_k=2, inter=256),
+    # shared expert twice as wide as the routed ones: two h units per lane on the down side
+    MoEConfig("few_wide_shared", tokens=5, hidden=512, experts=16, top_k=4, inter=256, shared_inter=512),
+    # e2m3 on a 1536-wide layer
+    MoEConfig("few_e2m3", tokens=4, hidden=1536, experts=32, top_k=4, inter=512, shared_inter=256, fmt=2),
+    # top-32 of 64 with 16 tokens and a shared expert: all 528 pair positions in use
+    MoEConfig("few_k32", tokens=16, hidden=256, experts=64, top_k=32, inter=128, shared_inter=128),
+]
+
+
+@pytest.mark.parametrize("same_logits", [False, True], ids=["own_logits", "same_logits"])
+@pytest.mark.parametrize("cfg", FEW_TOKEN_SHAPES, ids=lambda c: c.name)
+def test_few_token_kernel_shapes(cfg, same_logits):
+    """Shapes that take the 2-16 token kernel's less common paths (several
+    token batches per group when every token picks the same experts, wide
+    rows, a wide shared expert, the largest pair count): routing bit-exact and
+    outputs within tolerance of the oracle, and every token bitwise equal to
+    the same token decoded alone."""
+    require_gpu()
+    L = _layer(cfg)
+    T = cfg.tokens
+    x, l = _inputs(cfg, T, sub=9)
+    if same_logits:
+        l[:] = l[0]
+    xd, ld = dev_bf16(x), torch.from_numpy(l).cuda()
+    ws = moeq.workspace(L, T)
+    idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    out = moeq.moe_layer_decode(L, xd, ld, idx_out=idx, flags=F32, ws=ws)
+    ridx, _, ref = oracle_layer(cfg, x, l)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_rel_err(out.cpu().numpy(), ref) <= PARITY_TOL
+    for t in (0, T - 1):
+        one = moeq.moe_layer_decode(L, xd[t:t + 1], ld[t:t + 1], flags=F32, ws=ws)
+        assert torch.equal(one[0], out[t]), t
+    assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
