@@ -115,11 +115,17 @@ static hipError_t gemv_reg_go(const uint8_t *codes, const uint8_t *scales, int r
 // loads are served sooner take more rows and all finish together.  The
 // arithmetic of a row is the register-streamed kernel's (same lanes, units,
 // order and reduction), so every token's result is the same for any batch.
-constexpr int GL_NW = 16, GL_THREADS = 64 * GL_NW, GL_XT = 8;
+constexpr int GL_XT = 8;
 constexpr size_t GL_LDS = 100 * 1024;
+// Waves per workgroup and rows per item (each x unit read from LDS once for
+// all rows of an item).  Measured at B = 4 on the 25600 x 5120 e2m3 matrix:
+// 16 waves, 1 row 34.6 us; 16 waves, 2 rows 57.8; 8 waves, 2 rows 38.6;
+// 8 waves, 4 rows 58.9 (more rows per item cost registers, not LDS time).
+constexpr int GL_NW = 16;
+constexpr int GL_RX = 1;
 
-template <int FMT, int DEC, int Q, int R>
-__global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__restrict__ codes,
+template <int FMT, int DEC, int Q, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_lds_kernel(const uint8_t *__restrict__ codes,
                                                         const uint8_t *__restrict__ scales, int rows, int cols,
                                                         const uint16_t *__restrict__ x, int B, void *__restrict__ y,
                                                         int out_f32, int xt) {
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__r
         s_next[0] = 0;
         s_next[1] = 0;
     }
-    build_luts<FMT>(L, tid, GL_THREADS, DEC == DEC_LUT);
+    build_luts<FMT>(L, tid, 64 * NW, DEC == DEC_LUT);
 
     const int U = cols / 32, LPR = lanes_per_row(U), RPW = WAVE / LPR;
     const int lr = lane & (LPR - 1), rs = lane / LPR;
@@ -170,38 +176,47 @@ __global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__r
             }
         };
         auto compute = [&](int st, int it) {
+            float acc[R][GL_XT];
 #pragma unroll
-            for (int b = 0; b < R; ++b) {
-                float acc[GL_XT];
+            for (int b = 0; b < R; ++b)
 #pragma unroll
-                for (int t = 0; t < GL_XT; ++t) acc[t] = 0.f;
+                for (int t = 0; t < GL_XT; ++t) acc[b][t] = 0.f;
 #pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    const int u = lr + LPR * q;
-                    u32 wd[16];
-                    decode_unit<FMT, DEC>(un[st][b][q], L, wd);
-                    float s0, s1;
-                    unit_scales<FMT>(un[st][b][q], L, s0, s1);
-                    const uint4 *xb = reinterpret_cast<const uint4 *>(s_x + (u < U ? u : 0) * US);
+            for (int q = 0; q < Q; ++q) {
+                const int u = lr + LPR * q;
+                // this lane's unit of each row, decoded once; each x unit read once for all rows
+                u32 wd[R][16];
+                float s0[R], s1[R];
 #pragma unroll
-                    for (int t = 0; t < GL_XT; ++t) {
-                        if (t < mb) {
-                            u32 xv[16];
+                for (int b = 0; b < R; ++b) {
+                    decode_unit<FMT, DEC>(un[st][b][q], L, wd[b]);
+                    unit_scales<FMT>(un[st][b][q], L, s0[b], s1[b]);
+                }
+                const uint4 *xb = reinterpret_cast<const uint4 *>(s_x + (u < U ? u : 0) * US);
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const uint4 A = xb[4 * t + v];
-                                xv[4 * v] = A.x; xv[4 * v + 1] = A.y; xv[4 * v + 2] = A.z; xv[4 * v + 3] = A.w;
-                            }
-                            const float d = unit_dot<FMT>(wd, xv, s0, s1, acc[t]);
-                            acc[t] = u < U ? d : acc[t];
+                for (int t = 0; t < GL_XT; ++t) {
+                    if (t < mb) {
+                        u32 xv[16];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const uint4 A = xb[4 * t + v];
+                            xv[4 * v] = A.x; xv[4 * v + 1] = A.y; xv[4 * v + 2] = A.z; xv[4 * v + 3] = A.w;
+                        }
+#pragma unroll
+                        for (int b = 0; b < R; ++b) {
+                            const float d = unit_dot<FMT>(wd[b], xv, s0[b], s1[b], acc[b][t]);
+                            acc[b][t] = u < U ? d : acc[b][t];
                         }
                     }
                 }
+            }
+#pragma unroll
+            for (int b = 0; b < R; ++b) {
                 const int j = jrow(it, b);
 #pragma unroll
                 for (int t = 0; t < GL_XT; ++t) {
                     if (t < mb) {
-                        const float v = group_sum_dpp(acc[t], LPR);
+                        const float v = group_sum_dpp(acc[b][t], LPR);
                         if (j < nrow && lr == 0) {
                             const int64_t o = (int64_t)(t0 + t) * rows + r0 + j;
                             if (out_f32) reinterpret_cast<float *>(y)[o] = v;
@@ -218,7 +233,7 @@ __global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__r
         if (tid == 0) s_next[(nb + 1) & 1] = 0;
         int ia = grab();
         issue(0, ia);   // the weights do not depend on x: in flight while x is staged
-        for (int q = tid; q < mb * U * 4; q += GL_THREADS) {
+        for (int q = tid; q < mb * U * 4; q += 64 * NW) {
             const int t = q / (U * 4), rem = q - t * (U * 4), u = rem >> 2, v = rem & 3;
             const uint4 val = *reinterpret_cast<const uint4 *>(x + (int64_t)(t0 + t) * cols + 32 * u + 8 * v);
             *reinterpret_cast<uint4 *>(s_x + u * US + 16 * t + 4 * v) = val;
@@ -241,8 +256,8 @@ __global__ __launch_bounds__(GL_THREADS) void gemv_lds_kernel(const uint8_t *__r
 template <int FMT, int DEC, int Q>
 static hipError_t gemv_lds_go(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x, int B,
                               void *y, int out_f32, hipStream_t s) {
-    constexpr int R = (Q >= 2) ? 1 : 2;
-    auto kern = gemv_lds_kernel<FMT, DEC, Q, R>;
+    constexpr int R = (Q >= 2) ? GL_RX : 2 * GL_RX;
+    auto kern = gemv_lds_kernel<FMT, DEC, Q, R, GL_NW>;
     const int U = cols / 32;
     int xt = std::min(B, GL_XT);
     while (xt > 1 && (size_t)U * (16 * xt + 4) * 4 > GL_LDS) --xt;
@@ -257,7 +272,7 @@ static hipError_t gemv_lds_go(const uint8_t *codes, const uint8_t *scales, int r
     const int RPW = WAVE / lanes_per_row(U);
     // one workgroup per CU, at least a few rows per wave
     const int G = std::max(1, std::min(num_cus(), rows / (4 * GL_NW * RPW)));
-    hipLaunchKernelGGL(kern, dim3(G), dim3(GL_THREADS), dyn, s, codes, scales, rows, cols, x, B, y, out_f32, xt);
+    hipLaunchKernelGGL(kern, dim3(G), dim3(64 * GL_NW), dyn, s, codes, scales, rows, cols, x, B, y, out_f32, xt);
     return hipGetLastError();
 }
 
