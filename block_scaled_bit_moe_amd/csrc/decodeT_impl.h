@@ -8,16 +8,17 @@
 //   A. route every token (wave t routes token t) and build the expert groups
 //      in LDS (ascending expert id, tokens ascending inside an expert, the
 //      shared expert last with every token);
-//   B. gate | up: the groups' row indices (group-major) are split into G equal
-//      ranges; a workgroup walks its range one group at a time, with the
-//      group's tokens (up to DT_XT per batch) in LDS, streams each gate row and
+//   B. gate | up: the groups' row pairs (group-major) are split into G shares
+//      of equal cost (a row pair of a group with m tokens costs its weight
+//      bytes plus m dot products); a workgroup walks its share one group at a
+//      time, with the group's tokens (up to DT_XT per batch) in LDS, deals the
+//      row pairs to its waves from an LDS counter, streams each gate row and
 //      its up row through one lane group, and publishes h of every (token,
 //      row) as a 64-bit word (call tag << 32 | fp32 bits);
-//   C. down: the groups' output rows (group-major) are split into G equal
-//      ranges; per group, the workgroup reads that group's h for a token batch
-//      (tagged words, read again until every tag is current) into LDS as bf16
-//      hi/lo pairs, streams its down rows and publishes the partial outputs as
-//      tagged words;
+//   C. down: the groups' output rows are split the same way; per group, the
+//      workgroup reads that group's h for a token batch (tagged words, read
+//      again until every tag is current) into LDS as bf16 hi/lo pairs, streams
+//      its down rows and publishes the partial outputs as tagged words;
 //   D. combine: workgroup w owns output rows [w*RW, (w+1)*RW) of every token
 //      and sums the partials of the token's experts in rank order (plus the
 //      shared expert) once all their tags are current, then rounds once.
@@ -41,11 +42,10 @@ constexpr size_t DT_LDS = 112 * 1024;            // dynamic LDS: one batch's x (
 constexpr int DT_MAX_GROUPS = DEC_MAX_T * 32 + 1;
 constexpr int DT_HPT = 8;                         // h pieces per thread per read pass (phase C)
 
-// Rows per lane group and pass (gate/up: row pairs), so that every lane has
+// Rows per lane group and item (gate/up: row pairs), so that every lane has
 // several unit loads in flight in each of the two pipeline stages.
 __host__ __device__ constexpr int dt_rows_gu(int QG) { return QG >= 2 ? 1 : 2; }
 __host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 1 : 2; }
-constexpr int DT_STAGES_DN = 2;   // items in flight per wave on the down side (2 or 3)
 
 // Relative cost of one row (gate/up: one row pair) of a group with m tokens:
 // streaming its weights plus m dot products.  The static split of each phase
@@ -88,7 +88,7 @@ struct DTShared {
     unsigned char p_tok[DEC_MAX_PAIRS];   // token of each pair position
     short pos_of[DEC_MAX_T][33];          // pair position of (token, rank); rank k: the shared expert
     int scan[2 * DT_NW];
-    int n_groups, n_routed_groups;
+    int n_groups;
     u32 tag;
     int next[2];                          // work counters of even / odd batches
     int cum_gu[DT_MAX_GROUPS + 1];        // cost of the groups before g (gate/up, down)
@@ -223,7 +223,6 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
             }
         }
         if (tid == 0) {
-            S.n_routed_groups = nf;
             S.n_groups = nf + (Ish > 0 ? 1 : 0);
             int cg = I * (gu0 * nf + gu1 * nc), cd = H * (dn0 * nf + dn1 * nc);
             if (Ish > 0) {
@@ -405,7 +404,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
             auto jrow = [&](int it, int b) { return (it * RD + b) * RPWd + rsd; };
             for (int tb = 0; tb < m; tb += plan.xt_dn) {
                 const int mb = min(plan.xt_dn, m - tb);
-                Unit<FMT> un[DT_STAGES_DN][RD][QD];
+                Unit<FMT> un[2][RD][QD];
                 auto issue = [&](int st, int p) {
 #pragma unroll
                     for (int b = 0; b < RD; ++b) {
@@ -521,34 +520,15 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                         }
                     }
                 };
-                if constexpr (DT_STAGES_DN == 2) {
-                    for (;;) {
-                        const int ib = grab();
-                        issue(1, ib);
-                        if (ia >= nitem) break;
-                        compute(0, ia);
-                        ia = grab();
-                        issue(0, ia);
-                        if (ib >= nitem) break;
-                        compute(1, ib);
-                    }
-                } else {
-                    int ib = grab();
+                for (;;) {
+                    const int ib = grab();
                     issue(1, ib);
-                    for (;;) {
-                        const int ic = grab();
-                        issue(2, ic);
-                        if (ia >= nitem) break;
-                        compute(0, ia);
-                        ia = grab();
-                        issue(0, ia);
-                        if (ib >= nitem) break;
-                        compute(1, ib);
-                        ib = grab();
-                        issue(1, ib);
-                        if (ic >= nitem) break;
-                        compute(2, ic);
-                    }
+                    if (ia >= nitem) break;
+                    compute(0, ia);
+                    ia = grab();
+                    issue(0, ia);
+                    if (ib >= nitem) break;
+                    compute(1, ib);
                 }
                 ++nbatch;
             }
@@ -628,12 +608,16 @@ static hipError_t decodeT_go(const DecodeArgs &a, hipStream_t s) {
         --xt_dn;
     if (xt_gu < 1 || xt_dn < 1) return hipErrorNotSupported;
     const size_t dyn = std::max(dt_lds_bytes(L.H / 32, 16, xt_gu), dt_lds_bytes(Imax / 32, 32, xt_dn));
-    static size_t dyn_set = 0;   // per instantiation: dynamic LDS beyond the default limit
-    if (dyn > dyn_set) {
+    // per instantiation and device: dynamic LDS beyond the default limit
+    static size_t dyn_set[64] = {};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (dyn > dyn_set[dev]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
-        dyn_set = dyn;
+        dyn_set[dev] = dyn;
     }
     int cus = 0;
     const int cap = d1_coresident(kern, dyn, cus);

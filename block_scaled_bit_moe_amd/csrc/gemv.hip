@@ -262,12 +262,16 @@ static hipError_t gemv_lds_go(const uint8_t *codes, const uint8_t *scales, int r
     int xt = std::min(B, GL_XT);
     while (xt > 1 && (size_t)U * (16 * xt + 4) * 4 > GL_LDS) --xt;
     const size_t dyn = (size_t)U * (16 * xt + 4) * 4;
-    static size_t dyn_set = 0;   // per instantiation: dynamic LDS beyond the default limit
-    if (dyn > dyn_set) {
-        const hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    // per instantiation and device: dynamic LDS beyond the default limit
+    static size_t dyn_set[64] = {};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (dyn > dyn_set[dev]) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
-        dyn_set = dyn;
+        dyn_set[dev] = dyn;
     }
     const int RPW = WAVE / lanes_per_row(U);
     // one workgroup per CU, at least a few rows per wave
