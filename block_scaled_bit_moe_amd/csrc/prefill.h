@@ -125,21 +125,52 @@ __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
         for (int t = tid; t < T; t += PF_THREADS) list[t] = t;
         count = T;
     } else if (a.mode == MODE_ROUTE) {
-        for (int t0 = 0; t0 < T; t0 += PF_THREADS) {
-            const int t = t0 + tid;
-            int r = -1;
-            if (t < T) {
-                const int32_t *row = a.idx + (size_t)t * k;
-                for (int j = 0; j < k; ++j)
-                    if (row[j] == slot) r = j;
+        // Wave w scans the index words of tokens [w * span, (w + 1) * span),
+        // 64 consecutive words per load (coalesced, 16 loads in flight); a word equal to this slot
+        // is the hit of token word / k at rank word % k (a token picks a slot
+        // at most once), and the words are in token order, so a ballot gives
+        // each hit its place among the wave's hits.  Pass 1 counts, one
+        // barrier gives the four waves' bases, pass 2 (the words again, from
+        // L2) writes the list in ascending token order.
+        const int wv = tid >> 6, lane = tid & 63;
+        const int span = (T + 3) / 4;
+        const int d0 = min(T, wv * span) * k, d1 = min(T, (wv + 1) * span) * k;
+        constexpr int UNR = 16;   // loads in flight per lane
+        int mine = 0;
+        for (int d = d0; d < d1; d += 64 * UNR) {
+            int v[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int dd = d + 64 * u + lane;
+                v[u] = dd < d1 ? a.idx[dd] : -1;
             }
-            int total;
-            const int pos = count + pf_block_scan(r >= 0 ? 1 : 0, s_tmp, tid, total);
-            if (r >= 0) {
-                list[pos] = t;
-                a.rank[(size_t)t * k + r] = pos;
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) mine += __popcll(__ballot(v[u] == slot));
+        }
+        if (lane == 0) s_tmp[wv] = mine;
+        __syncthreads();
+        int pos = 0;
+        for (int w = 0; w < wv; ++w) pos += s_tmp[w];
+        count = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+        for (int d = d0; d < d1; d += 64 * UNR) {
+            int v[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int dd = d + 64 * u + lane;
+                v[u] = dd < d1 ? a.idx[dd] : -1;
             }
-            count += total;
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const uint64_t hit = __ballot(v[u] == slot);
+                if (v[u] == slot) {
+                    const int dd = d + 64 * u + lane;
+                    const int t = dd / k, r = dd - t * k;
+                    const int p = pos + (int)__popcll(hit & ((1ull << lane) - 1ull));
+                    list[p] = t;
+                    a.rank[(size_t)t * k + r] = p;
+                }
+                pos += (int)__popcll(hit);
+            }
         }
     }
     // publish the count; the last workgroup to arrive builds the plan
