@@ -12,7 +12,7 @@
 //   gate/up  per (block, tile of 64 intermediate rows): g = Wg x, u = Wu x
 //            on MFMA 16x16x32 bf16 with fp32 accumulation, then
 //            h = silu(g) * u, stored as a bf16 hi + lo pair
-//   down     per (block, tile of 512 hidden rows): y = Wd (h_hi + h_lo)
+//   down     per (block, tile of 512 hidden rows, 256 for e2m3): y = Wd (h_hi + h_lo)
 //            into fp32 partials, one row per (token, expert) pair
 //   combine  per token: sum of w_r * y_r in rank order, plus the shared
 //            expert, rounded once to bf16
@@ -52,7 +52,9 @@ constexpr int PF_KS = 128;                  // K per step
 constexpr int PF_ROW = PF_KS * 2 + 16;      // bytes per staged activation row
 constexpr int PF_STAGE = PF_MB * PF_ROW;    // bytes per staged plane
 constexpr int PF_RG_GU = 1;                 // 16-row groups per wave: gate/up (each of gate and up)
-constexpr int PF_RG_DN = 4;                 // down (measured: 2 -> 4 took 10 us off the 2,048-token layer)
+// down: e2m1 takes four (measured: 2 -> 4 took 10 us off the 2,048-token
+// layer); e2m3's larger units would spill registers with four
+template <int FMT> constexpr int pf_rg_dn() { return FMT == FMT_E2M1 ? 4 : 2; }
 constexpr int PF_PD = 3;                    // weight units in flight per row group (K steps ahead)
 constexpr int PF_MAX_K = 32;                // top-k limit of the layer
 
@@ -479,11 +481,12 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
 }
 
 // Grouped GEMM over the block list.  gate/up (DOWN = false): 4 waves, each
-// with 16 rows of gate and the same 16 rows of up; down: 8 waves of 64 rows.
+// with 16 rows of gate and the same 16 rows of up; down: 8 waves of 64 rows
+// (e2m1) or 32 rows (e2m3).
 template <int FMT, bool DOWN>
 __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel(PfArgs a, int NT) {
     constexpr int NWAVES = DOWN ? 8 : 4;
-    constexpr int RG = DOWN ? PF_RG_DN : PF_RG_GU;
+    constexpr int RG = DOWN ? pf_rg_dn<FMT>() : PF_RG_GU;
     constexpr int NB = DOWN ? RG : 2 * RG;
     constexpr int NPL = DOWN ? 2 : 1;
     constexpr int ROWS_WG = NWAVES * 16 * RG;

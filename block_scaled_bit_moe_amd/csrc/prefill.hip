@@ -55,7 +55,7 @@ size_t prefill_workspace_bytes(int T, int H, int I, int Ish, int k, int E) {
 template <int FMT>
 static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     const int Imax = p.L.I > p.L.Ish ? p.L.I : p.L.Ish;
-    const int rows_gu = 4 * 16 * PF_RG_GU, rows_dn = 8 * 16 * PF_RG_DN;   // weight rows per workgroup
+    const int rows_gu = 4 * 16 * PF_RG_GU, rows_dn = 8 * 16 * pf_rg_dn<FMT>();   // weight rows per workgroup
     const int nt_gu = (Imax + rows_gu - 1) / rows_gu;
     const int nt_dn = (p.L.H + rows_dn - 1) / rows_dn;
     hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
