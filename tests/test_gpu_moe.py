@@ -258,6 +258,8 @@ FEW_TOKEN_SHAPES = [
     MoEConfig("few_e2m3", tokens=4, hidden=1536, experts=32, top_k=4, inter=512, shared_inter=256, fmt=2),
     # top-32 of 64 with 16 tokens and a shared expert: all 528 pair positions in use
     MoEConfig("few_k32", tokens=16, hidden=256, experts=64, top_k=32, inter=128, shared_inter=128),
+    # the largest expert count: sixteen logits per lane in the routing wave
+    MoEConfig("few_e1024", tokens=6, hidden=256, experts=1024, top_k=10, inter=128, shared_inter=128),
 ]
 
 
@@ -285,4 +287,24 @@ def test_few_token_kernel_shapes(cfg, same_logits):
     for t in (0, T - 1):
         one = moeq.moe_layer_decode(L, xd[t:t + 1], ld[t:t + 1], flags=F32, ws=ws)
         assert torch.equal(one[0], out[t]), t
+    assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
+
+
+def test_calls_of_every_kernel_share_one_workspace():
+    """Calls of 1, 3 and 16 tokens (the single-token, few-token kernels) in a
+    mixed order on one workspace: every output bitwise equal to the same call
+    on a fresh workspace, so the call tag one kernel leaves behind never lets
+    another take a stale word as current."""
+    require_gpu()
+    cfg = SMALL
+    L = _layer(cfg)
+    x, l = _inputs(cfg, 16, sub=11)
+    xd, ld = dev_bf16(x), torch.from_numpy(l).cuda()
+    fresh = {}
+    for T in (1, 3, 16):
+        fresh[T] = moeq.moe_layer_decode(L, xd[:T], ld[:T], flags=F32, ws=moeq.workspace(L, 16))
+    ws = moeq.workspace(L, 16)
+    for T in (3, 1, 3, 16, 1, 16, 3, 1):
+        out = moeq.moe_layer_decode(L, xd[:T], ld[:T], flags=F32, ws=ws)
+        assert torch.equal(out, fresh[T]), T
     assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
