@@ -2,12 +2,19 @@
 
 A step is one call of moe_layer_decode on one batch of synthetic input: route,
 group by expert, gate | up, SiLU-multiply, down, combine -- the whole hot path.
-Inputs are resident in HBM before the timed region starts.  To defeat the
-256 MB last-level cache, the layer is replicated R times and every step uses
-the next replica and a fresh set of router logits (so it selects different
-experts).  The K timed steps are captured once in a HIP graph and replayed, so
-the figure is GPU time, not Python launch overhead; the eager figure is
-reported beside it.
+The default workload is the largest decode layer that fits one GPU: 16 tokens,
+hidden 6144, 288 experts, top-8, intermediate 2048.  Inputs are resident in HBM
+before the timed region starts.  To defeat the 256 MB last-level cache, every
+step uses a fresh set of router logits (so it selects different experts), the
+layer is replicated until the replicas hold >= 4 GiB, and a shared expert gets
+its own copy per logit set (so it is re-read only after >= 1 GB of other
+weights).  The K timed steps are captured once in a HIP graph; the graph is
+replayed enough times to fill a window of >= 50 ms, and the figure is the
+median of 5 such windows (GPU time, launch gaps between the graph's kernels
+included).  The same K calls launched eagerly from Python are timed the same
+way and reported as eager_ms_per_step.  The oracle runs on the host cores on a
+bounded sample, on all threads and on one, and the last timed output is
+compared with it (relative L2 and max relative error of the bf16 output).
 
 Prints one JSON line.  --config picks another workload (toy_decode,
 dense_gemv_e2m3, wide_decode, batched_decode, prefill).
@@ -37,7 +44,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
-DEFAULT_CONFIG = "wide_decode"
+DEFAULT_CONFIG = "batched_decode"
 COPY_BYTES = 512 << 20           # calibration copy: reads and writes this many bytes
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -60,7 +67,6 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0: enough for >= 4x the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     p.add_argument("--profile-steps", type=int, default=0,
                    help="only run this many eager steps after warmup, then the calibration copy "
                         "(for rocprofv3 counter runs)")
@@ -205,30 +211,72 @@ class Timer:
         return self.e0.elapsed_time(self.e1) * 1e-3      # seconds
 
 
-def run_steps(torch, calls, steps, warmup, eager):
-    """Time `steps` calls (cycling through `calls`) after `warmup` untimed ones."""
+WINDOW_S = 0.05     # each timed window lasts at least this long
+WINDOWS = 5         # windows per figure; the median is reported
+
+
+def _windows(torch, run_once, per_run_guess):
+    """Median over WINDOWS windows of the time of one `run_once()`; each window
+    repeats it enough times to last >= WINDOW_S.  Returns (median seconds per
+    run, repeats per window)."""
+    reps = max(1, int(np.ceil(WINDOW_S / max(per_run_guess, 1e-7))))
+    t = Timer(torch)
+    per = []
+    for _ in range(WINDOWS):
+        t.start()
+        for _ in range(reps):
+            run_once()
+        per.append(t.stop() / reps)
+    return float(np.median(per)), reps
+
+
+def run_steps(torch, calls, steps, warmup):
+    """Per-step seconds of `steps` calls (cycling through `calls`) after
+    `warmup` untimed ones, two ways: the `steps` calls captured once in a HIP
+    graph and replayed (GPU time, launch gaps inside the graph included), and
+    the same calls launched eagerly from Python (adds the binding's per-call
+    host cost).  Each figure is the median of WINDOWS windows of >= WINDOW_S."""
     n = len(calls)
     for i in range(warmup):
         calls[i % n]()
     torch.cuda.synchronize()
     seq = [calls[(warmup + i) % n] for i in range(steps)]
-    t = Timer(torch)
-    if eager:
-        t.start()
+
+    def eager():
         for c in seq:
             c()
-        return t.stop(), "eager"
+
+    t = Timer(torch)
+    t.start()
+    eager()
+    guess = t.stop()
+    eager_s, eager_reps = _windows(torch, eager, guess)
+
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            for c in seq:
-                c()
+            eager()
     torch.cuda.synchronize()
     g.replay()                      # one untimed replay
     t.start()
     g.replay()
-    return t.stop(), "hipgraph"
+    guess = t.stop()
+    graph_s, graph_reps = _windows(torch, g.replay, guess)
+    return {"per_step": graph_s / steps, "eager_per_step": eager_s / steps, "graph_replays_per_window": graph_reps,
+            "eager_repeats_per_window": eager_reps, "windows": WINDOWS}
+
+
+def err_figures(got_bf16_bits, ref):
+    """S13(iii)-style figures of a bf16 output against the double oracle: the
+    relative L2 error and the unadjusted max relative error (informational;
+    the parity bar is on the fp32 output, in the tests)."""
+    import oracle
+    got = np.array([oracle.bf16_value(int(b)) for b in np.asarray(got_bf16_bits).ravel()]).reshape(ref.shape)
+    rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    nz = np.abs(ref) > 0
+    max_rel = float(np.max(np.abs(got - ref)[nz] / np.abs(ref)[nz])) if nz.any() else 0.0
+    return {"rel_l2": rel_l2, "max_rel_unadjusted": max_rel, "elements": int(ref.size)}
 
 
 def cpu_baseline_moe(cfg, seconds, logits_list, x, slice_tokens=None):
@@ -265,6 +313,19 @@ def cpu_baseline_moe(cfg, seconds, logits_list, x, slice_tokens=None):
     return tokens, spent
 
 
+def cpu_figures(run_sample, seconds, cores):
+    """The oracle timed on all `cores` threads (~`seconds`) and on one thread
+    (~seconds / 2).  run_sample(budget) returns (work units done, seconds,
+    sample text).  Returns the cpu_baseline dict's parts."""
+    import oracle
+    oracle.set_threads(cores)
+    n_all, el_all, what_all = run_sample(seconds)
+    oracle.set_threads(1)
+    n_one, el_one, what_one = run_sample(seconds / 2)
+    oracle.set_threads(cores)
+    return (n_all / el_all, what_all), (n_one / el_one, what_one)
+
+
 def main():
     a = parse()
     if a.traffic_summary:
@@ -287,7 +348,7 @@ def main():
     cfg = configs.ALL[a.config]
     cores = len(os.sched_getaffinity(0))
     omp = int(os.environ.get("OMP_NUM_THREADS", cores))
-    result = {}
+    errs = None
 
     if isinstance(cfg, configs.GemvConfig):
         B = a.batch
@@ -299,7 +360,8 @@ def main():
         for r in range(R):
             cc, ss = (base_c, base_s) if r == 0 else (base_c.clone(), base_s.clone())
             Ws.append(moeq.QMat(cfg.fmt, cfg.rows, cfg.cols, cc, ss))
-        x = dev_bf16(synth.gemv_x(cfg, B))
+        xg = synth.gemv_x(cfg, B)
+        x = dev_bf16(xg)
         y = torch.empty((B, cfg.rows), dtype=torch.bfloat16, device="cuda")
         calls = [(lambda W=W: moeq.dense_gemv_q(W, x, y=y)) for W in Ws]
         if a.profile_steps:
@@ -308,29 +370,32 @@ def main():
             torch.cuda.synchronize()
             copy_calibration(torch)
             return
-        secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
-        per = secs / a.steps
+        tm = run_steps(torch, calls, a.steps, a.warmup)
+        per = tm["per_step"]
         tokens_per_s = B / per
         achieved = wbytes / per / 1e9
         metric_value = tokens_per_s
         workload = {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols, "batch": B, "fmt": "e2m3+ue8m0/128",
                     "replicas": R}
         kernel = kernel_of(cfg.name, B)
+        import oracle
+        rows = np.arange(0, cfg.rows, 97)
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[:, rows]
+        errs = err_figures(yb, oracle.gemv(cfg.fmt, cfg.rows, cfg.cols, c, s, xg, row_list=rows))
+        errs["sample"] = "every 97th row of the last timed call"
         cpu = None
         if not a.no_cpu_baseline:
-            import oracle
             n_rows = 256
-            t0 = time.perf_counter()
-            reps = 0
-            while time.perf_counter() - t0 < a.cpu_seconds:
-                oracle.gemv(cfg.fmt, cfg.rows, cfg.cols, c, s, synth.gemv_x(cfg, B), row_list=np.arange(n_rows) + reps)
-                reps += 1
-            el = time.perf_counter() - t0
-            frac = reps * n_rows / cfg.rows
-            cpu = {"value": B * frac / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
-                   "sample": "%d row blocks of %d rows (%.4f of the matrix) x B=%d, scaled to whole GEMVs" %
-                             (reps, n_rows, frac, B),
-                   "weight_GBps": frac * wbytes / el / 1e9}
+
+            def sample(budget):
+                t0, reps = time.perf_counter(), 0
+                while time.perf_counter() - t0 < budget:
+                    oracle.gemv(cfg.fmt, cfg.rows, cfg.cols, c, s, xg, row_list=np.arange(n_rows) + reps)
+                    reps += 1
+                el = time.perf_counter() - t0
+                frac = reps * n_rows / cfg.rows
+                return B * frac, el, "%d row blocks of %d rows (%.4f of the matrix) x B=%d, scaled to whole GEMVs" % (
+                    reps, n_rows, frac, B)
     else:
         T = cfg.tokens
         many = T > moeq.MAX_DECODE_TOKENS
@@ -338,26 +403,26 @@ def main():
         layer_bytes = cfg.experts * per_expert
         R = a.replicas or max(1, min(32, -(-(4 << 30) // layer_bytes)))
         devs, shared = upload_layer_tensors(cfg)
-        L0 = moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, devs["w13_codes"],
-                        devs["w13_scales"], devs["w2_codes"], devs["w2_scales"],
-                        shared_inter=cfg.shared_inter, shared=shared)
-        layers = [L0]
+        names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
+        routed = [[devs[n] for n in names]]
         for r in range(1, R):
-            t = [tt.clone() for tt in L0.tensors[:4]]
-            sh = None
-            if cfg.shared_inter:
-                sh = dict(zip(("w13_codes", "w13_scales", "w2_codes", "w2_scales"), [tt.clone() for tt in L0.tensors[4:]]))
-            layers.append(moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, *t,
-                                     shared_inter=cfg.shared_inter, shared=sh))
+            routed.append([t.clone() for t in routed[0]])
         NL = 64 if not many else 4
+        # one copy of the shared expert per logit set: a call re-reads its
+        # shared expert only NL calls later (>= 1 GB of other weights between)
+        n_sh = NL if cfg.shared_inter else 0
+        shared_copies = [shared] + [{n: shared[n].clone() for n in names} for _ in range(n_sh - 1)] if n_sh else []
+        n = max(R, NL)
+        layers = [moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, *routed[i % R],
+                             shared_inter=cfg.shared_inter, shared=shared_copies[i % n_sh] if n_sh else None)
+                  for i in range(n)]
         logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
         logits = [torch.from_numpy(l).cuda() for l in logits_host]
         xh = synth.hidden_states(cfg)
         x = dev_bf16(xh)
-        ws = moeq.workspace(L0, T)
+        ws = moeq.workspace(layers[0], T)
         out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-        n = max(R, NL)
-        calls = [(lambda i=i: moeq.moe_layer_decode(layers[i % R], x, logits[i % NL], out=out, ws=ws))
+        calls = [(lambda i=i: moeq.moe_layer_decode(layers[i], x, logits[i % NL], out=out, ws=ws))
                  for i in range(n)]
         if a.profile_steps:
             for i in range(a.warmup + a.profile_steps):
@@ -366,9 +431,9 @@ def main():
             moeq.moe_workspace_status(ws)
             copy_calibration(torch)
             return
-        secs, mode = run_steps(torch, calls, a.steps, a.warmup, a.eager)
+        tm = run_steps(torch, calls, a.steps, a.warmup)
         moeq.moe_workspace_status(ws)
-        per = secs / a.steps
+        per = tm["per_step"]
         # algorithmic bytes: the packed codes + scales of every expert the call uses, read once
         used = [len(topk_sets(logits_host[(a.warmup + i) % NL], cfg.top_k)) + (1 if cfg.shared_inter else 0)
                 for i in range(a.steps)]
@@ -379,10 +444,9 @@ def main():
         metric_value = tokens_per_s
         workload = {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "experts": cfg.experts,
                     "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
-                    "fmt": "e2m1+e4m3/16", "replicas": R, "logit_sets": NL,
-                    "experts_read_per_call": float(np.mean(used))}
+                    "fmt": "e2m1+e4m3/16", "replicas": R, "logit_sets": NL, "shared_copies": n_sh,
+                    "experts_read_per_call": float(np.mean(used)), "weight_bytes_per_call": wbytes}
         kernel = kernel_of(cfg.name)
-        cpu = None
         if many:
             # the matrix-core work of the step: 2 flops per multiply-add of gate, up and down
             pairs = T * (cfg.top_k + (1 if cfg.shared_inter else 0))
@@ -392,11 +456,31 @@ def main():
             workload["pairs"] = pairs
             workload["mfma_tflops_algorithmic"] = flops / per / 1e12
             workload["mfma_frac_of_bf16_dense_peak"] = flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        # error figures of the last timed call's bf16 output against the oracle
+        # (all tokens; the first 16 of a many-token call)
+        last = (a.warmup + a.steps - 1) % n
+        outb = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        nt = min(T, 16)
+        import oracle
+        lg = logits_host[last % NL][:nt]
+        idx, _ = oracle.route(lg, cfg.top_k)
+        ex = {int(e): synth.expert_weights(cfg, int(e)) for e in np.unique(idx)}
+        sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
+        _, _, ref = oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xh[:nt], lg,
+                                 shared=sh, shared_inter=cfg.shared_inter)
+        errs = err_figures(outb[:nt], ref)
+        errs["sample"] = "%d token(s) of the last timed call" % nt
+        cpu = None
         if not a.no_cpu_baseline:
-            tok, el = cpu_baseline_moe(cfg, a.cpu_seconds, logits_host, xh, slice_tokens=16 if many else None)
-            cpu = {"value": tok / el, "unit": "tokens/s", "cores": omp, "kind": "oracle",
-                   "sample": "%d token(s) of the workload (%s, fresh logits); %.1f s of oracle time" %
-                             (tok, "slices of 16 tokens of the chunk" if many else "whole calls", el)}
+            def sample(budget):
+                tok, el = cpu_baseline_moe(cfg, budget, logits_host, xh, slice_tokens=16 if many else None)
+                return tok, el, "%d token(s) of the workload (%s, fresh logits); %.1f s of oracle time" % (
+                    tok, "slices of 16 tokens of the chunk" if many else "whole calls", el)
+
+    if not a.no_cpu_baseline:
+        (v_all, s_all), (v_one, s_one) = cpu_figures(sample, a.cpu_seconds, omp)
+        cpu = {"value": v_all, "unit": "tokens/s", "cores": omp, "kind": "oracle", "sample": s_all,
+               "single_thread": {"value": v_one, "unit": "tokens/s", "cores": 1, "sample": s_one}}
 
     traffic = measured_traffic(cfg.name, a.batch)
     line = {
@@ -407,16 +491,21 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": per * 1e3,
+        "eager_ms_per_step": tm["eager_per_step"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded generator; random-init weights of the workload's shapes)",
-        "config": dict(workload, launch=mode),
+        "config": dict(workload, launch="hipgraph", arithmetic="low-bit weights decoded exactly, bf16 activations, "
+                       "fp32 accumulate, bf16 output", graph_replays_per_window=tm["graph_replays_per_window"],
+                       eager_repeats_per_window=tm["eager_repeats_per_window"], windows=tm["windows"],
+                       window_min_ms=WINDOW_S * 1e3, statistic="median of windows"),
         "effective_weight_GBps": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel},
         "cpu_baseline": cpu,
+        "output_error_vs_oracle": errs,
     }
     print(json.dumps(line), flush=True)
 

@@ -59,7 +59,8 @@ def load_library(path=None):
     lib = ctypes.CDLL(p)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
-    lib.moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer), i32, ctypes.POINTER(sz)]
+    lib.moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(moe_layer), i32]
+    lib.moe_layer_workspace_bytes.restype = sz
     lib.moe_expert_ffn_q.argtypes = [ctypes.POINTER(moe_layer), i32, vp, i32, vp, i32, vp, sz, vp]
     lib.moe_layer_decode.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.dense_gemv_q.argtypes = [ctypes.POINTER(moe_qmat), vp, i32, vp, i32, vp]
@@ -67,8 +68,7 @@ def load_library(path=None):
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_version.restype = i32
-    for f in ("moe_route_topk", "moe_layer_workspace_bytes", "moe_expert_ffn_q", "moe_layer_decode",
-              "dense_gemv_q", "moe_workspace_status"):
+    for f in ("moe_route_topk", "moe_expert_ffn_q", "moe_layer_decode", "dense_gemv_q", "moe_workspace_status"):
         getattr(lib, f).restype = i32
     if path is None:
         _lib = lib
@@ -108,12 +108,36 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _U8 = (torch.uint8,)
 
 
+def _shape(t, name, shape):
+    """Refuse a tensor whose shape is not `shape` (the kernels would read or
+    write past its allocation)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _numel(t, name, n):
+    if t.numel() != n:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), n))
+
+
+def code_row_bytes(fmt, cols):
+    """Bytes of one row of codes of `cols` weights."""
+    return cols // 2 if fmt == MOE_FMT_E2M1_E4M3_B16 else cols * 3 // 4
+
+
+def scale_row_bytes(fmt, cols):
+    """Scale bytes of one row of `cols` weights."""
+    return cols // 16 if fmt == MOE_FMT_E2M1_E4M3_B16 else cols // 128
+
+
 class QMat:
     """A block-scaled matrix [rows][cols] on the GPU (codes and scales uint8)."""
 
     def __init__(self, fmt, rows, cols, codes, scales):
         self.fmt, self.rows, self.cols = fmt, rows, cols
         self.codes, self.scales = codes, scales
+        _numel(codes, "codes", rows * code_row_bytes(fmt, cols))
+        _numel(scales, "scales", rows * scale_row_bytes(fmt, cols))
         self.c = moe_qmat(fmt, rows, cols, 0, _dev(codes, "codes", _U8).value, _dev(scales, "scales", _U8).value)
 
 
@@ -128,9 +152,19 @@ class Layer:
         self.fmt, self.hidden, self.inter, self.n_experts, self.top_k = fmt, hidden, inter, n_experts, top_k
         self.shared_inter = shared_inter
         self.tensors = [w13_codes, w13_scales, w2_codes, w2_scales]
+        H, I, E = hidden, inter, n_experts
+        _numel(w13_codes, "w13_codes", E * 2 * I * code_row_bytes(fmt, H))
+        _numel(w13_scales, "w13_scales", E * 2 * I * scale_row_bytes(fmt, H))
+        _numel(w2_codes, "w2_codes", E * H * code_row_bytes(fmt, I))
+        _numel(w2_scales, "w2_scales", E * H * scale_row_bytes(fmt, I))
         sh = [None] * 4
         if shared_inter:
             names = ("w13_codes", "w13_scales", "w2_codes", "w2_scales")
+            Is = shared_inter
+            _numel(shared["w13_codes"], "shared w13_codes", 2 * Is * code_row_bytes(fmt, H))
+            _numel(shared["w13_scales"], "shared w13_scales", 2 * Is * scale_row_bytes(fmt, H))
+            _numel(shared["w2_codes"], "shared w2_codes", H * code_row_bytes(fmt, Is))
+            _numel(shared["w2_scales"], "shared w2_scales", H * scale_row_bytes(fmt, Is))
             sh = [_dev(shared[n], "shared " + n, _U8).value for n in names]
             self.tensors += [shared[n] for n in names]
         self.c = moe_layer(fmt, hidden, inter, n_experts, top_k, shared_inter,
@@ -156,6 +190,8 @@ def moe_route_topk(logits, k, idx=None, w=None):
         idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _shape(idx, "idx", (T, k))
+    _shape(w, "w", (T, k))
     _check(load_library().moe_route_topk(_dev(logits, "logits", (torch.float32,)), T, E, k,
                                          _dev(idx, "idx", (torch.int32,)), _dev(w, "w", (torch.float32,)),
                                          _stream()))
@@ -163,9 +199,10 @@ def moe_route_topk(logits, k, idx=None, w=None):
 
 
 def moe_layer_workspace_bytes(layer, T):
-    n = ctypes.c_size_t(0)
-    _check(load_library().moe_layer_workspace_bytes(ctypes.byref(layer.c), T, ctypes.byref(n)))
-    return n.value
+    n = load_library().moe_layer_workspace_bytes(ctypes.byref(layer.c), T)
+    if not n:
+        raise MoeError(MOE_EINVAL, moe_last_error())
+    return n
 
 
 def workspace(layer, T, device=None):
@@ -183,7 +220,9 @@ def _out(x, rows, cols, flags, out):
 def moe_expert_ffn_q(layer, expert, x, y=None, flags=0, ws=None):
     """One expert's SwiGLU FFN on the M rows of x (bf16 [M][H]); expert -1 = shared."""
     M = x.shape[0]
+    _shape(x, "x", (M, layer.hidden))
     y = _out(x, M, layer.hidden, flags, y)
+    _shape(y, "y", (M, layer.hidden))
     ws = workspace(layer, M, x.device) if ws is None else ws
     _check(load_library().moe_expert_ffn_q(ctypes.byref(layer.c), expert, _dev(x, "x", _BF16), M,
                                            _dev(y, "y", (torch.bfloat16, torch.float32)), flags,
@@ -194,7 +233,14 @@ def moe_expert_ffn_q(layer, expert, x, y=None, flags=0, ws=None):
 def moe_layer_decode(layer, x, logits, out=None, idx_out=None, w_out=None, flags=0, ws=None):
     """The MoE layer for the T rows of x: returns out [T][H] (bf16, or fp32 with MOE_OUT_F32)."""
     T = x.shape[0]
+    _shape(x, "x", (T, layer.hidden))
+    _shape(logits, "logits", (T, layer.n_experts))
     out = _out(x, T, layer.hidden, flags, out)
+    _shape(out, "out", (T, layer.hidden))
+    if idx_out is not None:
+        _shape(idx_out, "idx_out", (T, layer.top_k))
+    if w_out is not None:
+        _shape(w_out, "w_out", (T, layer.top_k))
     ws = workspace(layer, T, x.device) if ws is None else ws
     pi = _dev(idx_out, "idx_out", (torch.int32,)) if idx_out is not None else None
     pw = _dev(w_out, "w_out", (torch.float32,)) if w_out is not None else None
@@ -208,7 +254,9 @@ def moe_layer_decode(layer, x, logits, out=None, idx_out=None, w_out=None, flags
 def dense_gemv_q(W, x, y=None, flags=0):
     """y [B][rows] = W x[b] for x bf16 [B][cols]."""
     B = x.shape[0]
+    _shape(x, "x", (B, W.cols))
     y = _out(x, B, W.rows, flags, y)
+    _shape(y, "y", (B, W.rows))
     _check(load_library().dense_gemv_q(ctypes.byref(W.c), _dev(x, "x", _BF16), B,
                                        _dev(y, "y", (torch.bfloat16, torch.float32)), flags, _stream()))
     return y

@@ -14,6 +14,7 @@
 
 using namespace moeq;
 
+
 static thread_local char g_err[512];
 
 static int fail(int code, const char *fmt, ...) {
@@ -58,13 +59,13 @@ static int decoder_from_flags(int flags) {
 }
 
 int moeq::decoder_choice() {
-    static int choice = -1;
-    if (choice < 0) {
+    // read once (initialisation of a local static is thread-safe).  The
+    // hardware conversions are the default: they decode a unit in fewer
+    // instructions and leave LDS free; the table decoder stays selectable.
+    static const int choice = [] {
         const char *v = getenv("MOEQ_DECODER");
-        // The hardware conversions are the default: they decode a unit in fewer
-        // instructions and leave LDS free; the table decoder stays selectable.
-        choice = (v && !strcmp(v, "lut")) ? DEC_LUT : DEC_HW;
-    }
+        return (v && !strcmp(v, "lut")) ? DEC_LUT : DEC_HW;
+    }();
     return choice;
 }
 
@@ -157,13 +158,15 @@ int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float
     return ok();
 }
 
-int moe_layer_workspace_bytes(const moe_layer *L, int T, size_t *bytes) {
-    if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
-    CHECK(validate_layer(L));
-    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
-    CHECK(decode_supported(L, T));
-    *bytes = ws_need(L, T);
-    return ok();
+size_t moe_layer_workspace_bytes(const moe_layer *L, int T) {
+    if (validate_layer(L) != MOE_OK) return 0;
+    if (T < 1 || T > MOE_MAX_TOKENS) {
+        fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+        return 0;
+    }
+    if (decode_supported(L, T) != MOE_OK) return 0;
+    ok();
+    return ws_need(L, T);
 }
 
 static int check_ws(const moe_layer *L, int T, const void *ws, size_t ws_bytes) {

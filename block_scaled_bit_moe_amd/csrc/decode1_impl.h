@@ -44,7 +44,7 @@
 
 #include "kernels.h"
 #include "rowdot.h"
-#include "stream.h"
+#include "memops.h"
 
 namespace moeq {
 
@@ -467,19 +467,12 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
 
 namespace moeq {
 
+// Workgroups of `kernel` that can be resident at once on the current device
+// (cached per device and LDS size: no runtime query after the first call).
 template <typename K>
 static int d1_coresident(K kernel, size_t dyn_lds, int &cus) {
-    int dev = 0;
-    cus = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus <= 0) cus = 1;
-    int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void *>(kernel), D1_THREADS,
-                                                     dyn_lds) != hipSuccess ||
-        per <= 0)
-        per = 0;
-    return per * cus;
+    cus = cached_cus();
+    return cached_occupancy(reinterpret_cast<const void *>(kernel), D1_THREADS, dyn_lds) * cus;
 }
 
 // Try a launch with MG gate/up slots and MD down slots per wave; returns
@@ -507,10 +500,12 @@ static hipError_t decode1_try(const DecodeArgs &a, hipStream_t s) {
     if (nmax > D1_MAX_PAIRS_WG || nmax > D1_NW * (MG / 2) * RPWg) return hipErrorNotSupported;
     const int rw = (L.H + G - 1) / G;
     if (rw > D1_MAX_RW || NG * rw > D1_NW * MD * RPWd) return hipErrorNotSupported;
-    // floor(2^32 / rw) + 1: exact quotients for the small numerators used (checked)
+    // m = floor(2^32 / rw) + 1 = 2^32 / rw + f with 0 < f <= 1, so d * m / 2^32 =
+    // d / rw + d * f / 2^32 and the floor is exact while d * f / 2^32 < 1 / rw,
+    // i.e. for every d < 2^32 / rw: here d < 16 * 64 * MD (wave, lane group,
+    // slot) and rw <= 64, far below that
+    static_assert((uint64_t)D1_NW * 64 * MD * D1_MAX_RW < (1ull << 32), "magic division range");
     D1Plan plan{G, P, rw, (1ull << 32) / (uint64_t)rw + 1u, down_lanes_per_row(L.I, L.Ish)};
-    for (int v = 0; v < D1_NW * (MD + 1) * RPWd; ++v)
-        if ((int)(((uint64_t)v * plan.magic_rw) >> 32) != v / rw) return hipErrorNotSupported;
     hipLaunchKernelGGL(kern, dim3(G), dim3(D1_THREADS), dyn, s, a, plan);
     return hipGetLastError();
 }

@@ -612,17 +612,9 @@ static hipError_t decodeT_launch(const DecodeArgs &a, hipStream_t s) {
         --xt_dn;
     if (xt_gu < 1 || xt_dn < 1) return hipErrorNotSupported;
     const size_t dyn = std::max(dt_lds_bytes(L.H / 32, 16, xt_gu), dt_lds_bytes(Imax / 32, 32, xt_dn));
-    // per instantiation and device: dynamic LDS beyond the default limit
-    static size_t dyn_set[64] = {};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (dyn > dyn_set[dev]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (e != hipSuccess) return e;
-        dyn_set[dev] = dyn;
-    }
+    // dynamic LDS beyond the default limit (raised once per device)
+    const hipError_t le = ensure_dyn_lds(reinterpret_cast<const void *>(kern), dyn);
+    if (le != hipSuccess) return le;
     int cus = 0;
     const int cap = d1_coresident(kern, dyn, cus);
     const int G = std::min(cus, cap);   // every workgroup resident: they wait on each other

@@ -403,28 +403,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
+// Workgroups of `kernel` resident at once on the current device (cached).
 template <typename K>
 static int coresident_blocks(K kernel) {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (cus <= 0) cus = 1;
-    }
-    int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void *>(kernel), 256, 0) !=
-            hipSuccess ||
-        per <= 0)
-        per = 1;
-    return per * cus;
+    const int per = cached_occupancy(reinterpret_cast<const void *>(kernel), 256, 0);
+    return (per > 0 ? per : 1) * cached_cus();
 }
 
 template <int FMT, int DEC, int QG, int QD, int MT>
 static hipError_t decode_go(const DecodeArgs &a, hipStream_t s) {
     auto kern = decode_kernel<FMT, DEC, QG, QD, MT>;
-    static int cap = 0;   // per instantiation
-    if (!cap) cap = coresident_blocks(kern);
+    const int cap = coresident_blocks(kern);
     // upper bound of the item count: every pair its own group
     const LayerArgs &L = a.L;
     const int groups = (a.mode == MODE_ROUTE) ? ((a.T * L.k < L.E ? a.T * L.k : L.E) + (L.Ish > 0)) : 1;

@@ -21,16 +21,7 @@ namespace moeq {
 
 constexpr int GEMV_REG_WG_PER_CU = 2;   // one-token kernel: workgroups per CU (its occupancy)
 
-static int num_cus() {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (cus <= 0) cus = 1;
-    }
-    return cus;
-}
+static int num_cus() { return cached_cus(); }
 
 // Register-streamed variant: the x units stay in VGPRs, and each wave walks
 // its rows (every nw-th row group) R per pass with the next pass's loads in
@@ -262,17 +253,9 @@ static hipError_t gemv_lds_go(const uint8_t *codes, const uint8_t *scales, int r
     int xt = std::min(B, GL_XT);
     while (xt > 1 && (size_t)U * (16 * xt + 4) * 4 > GL_LDS) --xt;
     const size_t dyn = (size_t)U * (16 * xt + 4) * 4;
-    // per instantiation and device: dynamic LDS beyond the default limit
-    static size_t dyn_set[64] = {};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (dyn > dyn_set[dev]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (e != hipSuccess) return e;
-        dyn_set[dev] = dyn;
-    }
+    // dynamic LDS beyond the default limit (raised once per device)
+    const hipError_t le = ensure_dyn_lds(reinterpret_cast<const void *>(kern), dyn);
+    if (le != hipSuccess) return le;
     const int RPW = WAVE / lanes_per_row(U);
     // one workgroup per CU, at least a few rows per wave
     const int G = std::max(1, std::min(num_cus(), rows / (4 * GL_NW * RPW)));

@@ -74,4 +74,10 @@ hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s);
 
 int decoder_choice();    // DEC_LUT or DEC_HW (MOEQ_DECODER=lut|hw, read once)
 
+// Cached runtime queries (launch_cache.cpp), per device; thread-safe.
+int current_device();
+int cached_cus();                                                  // CUs of the current device
+int cached_occupancy(const void *kern, int threads, size_t dyn);   // resident workgroups per CU
+hipError_t ensure_dyn_lds(const void *kern, size_t dyn);           // allow `dyn` bytes of dynamic LDS
+
 }  // namespace moeq

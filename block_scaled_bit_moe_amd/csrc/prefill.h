@@ -37,7 +37,7 @@
 #include <type_traits>
 
 #include "common.h"
-#include "stream.h"
+#include "memops.h"
 
 namespace moeq {
 

@@ -41,48 +41,6 @@ __device__ inline void load_x_units(u32 (&xr)[Q][MT][16], const uint16_t *const 
     }
 }
 
-// acc[b][t] = row_b . x_t for R rows and MT tokens.  With SPLIT the activation
-// is an fp32 vector carried as bf16 hi + lo parts (xh, xl) and both are used.
-template <int FMT, int DEC, int Q, int MT, int R, bool SPLIT>
-__device__ inline void rows_dot(const uint8_t *const (&crow)[R], const uint8_t *const (&srow)[R], int U, int lr,
-                                int LPR, const u32 (&xh)[Q][MT][16], const u32 (&xl)[Q][MT][16], const Luts &L,
-                                float (&acc)[R][MT]) {
-    Unit<FMT> un[R][Q];
-#pragma unroll
-    for (int b = 0; b < R; ++b)
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int u = lr + LPR * q;
-            if (u < U) load_unit<FMT>(un[b][q], crow[b], srow[b], u);
-        }
-#pragma unroll
-    for (int b = 0; b < R; ++b)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[b][t] = 0.f;
-#pragma unroll
-    for (int b = 0; b < R; ++b) {
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int u = lr + LPR * q;
-            if (u < U) {
-                u32 w[16];
-                decode_unit<FMT, DEC>(un[b][q], L, w);
-                float s0, s1;
-                unit_scales<FMT>(un[b][q], L, s0, s1);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    if constexpr (SPLIT) acc[b][t] = unit_dot_split<FMT>(w, xh[q][t], xl[q][t], s0, s1, acc[b][t]);
-                    else acc[b][t] = unit_dot<FMT>(w, xh[q][t], s0, s1, acc[b][t]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < R; ++b)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[b][t] = group_sum_dpp(acc[b][t], LPR);
-}
-
 // Double-buffered row stream: passes of R rows per lane group, the loads of
 // pass p+1 in flight while pass p is decoded and multiplied.  `row(p, b,
 // &crow, &srow)` gives row b of pass p and returns its id, or -1 for a row

@@ -63,9 +63,10 @@
  *    is bit-exact: larger logit first, equal logits (+0 == -0) by lower expert
  *    index, NaN below every number.  A token's result does not depend on which
  *    other tokens share the call.
- *  - The library keeps no state between calls except constant tables.  Calls
- *    on different streams need different workspaces; they are otherwise
- *    reentrant.
+ *  - The library keeps no state between calls except facts about each device
+ *    that a launch needs (CU count, occupancy), looked up once and cached on
+ *    the host behind a lock.  Calls may come from several threads; calls on
+ *    different streams need different workspaces.
  */
 #ifndef MOEQ_H
 #define MOEQ_H
@@ -147,10 +148,17 @@ typedef struct moe_layer {
  * MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK). */
 int moe_route_topk(const float *logits, int T, int E, int k, int32_t *idx, float *w, void *stream);
 
-/* Bytes of workspace moe_layer_decode / moe_expert_ffn_q need for T tokens
- * (*bytes is host memory).  The workspace must be zeroed once after
- * allocation; the kernels leave its counters at zero on return. */
-int moe_layer_workspace_bytes(const moe_layer *L, int T, size_t *bytes);
+/* Bytes of workspace moe_layer_decode / moe_expert_ffn_q need for T tokens,
+ * or 0 when L or T breaks a rule (moe_last_error() then says which).  The
+ * workspace holds what the pages' engines keep between their expert kernels
+ * (Strata docs/INTEL.md, "The engine itself on Intel": the grouped work list,
+ * the gate | up results and the per-expert partial outputs before the
+ * combine) plus a small header of counters.  It must be zeroed once after
+ * allocation.  The header keeps a call counter that only grows (it tags the
+ * values exchanged between workgroups, so a value left by an earlier call is
+ * never taken for the current one) and an error word; every other counter is
+ * back at zero when a call's kernels end.  One workspace per stream. */
+size_t moe_layer_workspace_bytes(const moe_layer *L, int T);
 
 /* One expert's SwiGLU FFN on M rows of x (nextsycl README, "What it does":
  * gate | up, then down).
@@ -160,7 +168,10 @@ int moe_layer_workspace_bytes(const moe_layer *L, int T, size_t *bytes);
 int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void *y, int flags,
                      void *ws, size_t ws_bytes, void *stream);
 
-/* The whole layer for T tokens: route, group the (token, expert) pairs by
+/* The whole layer for T tokens (Strata docs/INTEL.md, "The engine itself on
+ * Intel": router_top10, the grouped expert kernels and the shared_expert
+ * kernel of one MoE layer; colibri README, "DeepSeek V4": routed experts plus
+ * one shared expert, top-k): route, group the (token, expert) pairs by
  * expert, run every selected expert once over its tokens, and combine
  *   out[t] = sum_{r<k} w[t][r] * FFN_{idx[t][r]}(x_t) + FFN_shared(x_t)
  * in that order.  idx_out (int32 [T][k]) and w_out (fp32 [T][k]) receive the
@@ -182,7 +193,10 @@ int dense_gemv_q(const moe_qmat *W, const void *x, int B, void *y, int flags, vo
  * MOE_OK, MOE_EKERNEL, or a negative validation/HIP code. */
 int moe_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
-/* Text of the last non-OK return on this thread ("" if none). */
+/* Text of the last non-OK return on this thread ("" if none): the failing
+ * argument and rule, or the HIP operation and its error (knivesysl README,
+ * "current benchmark": native errors name the operation and the device error,
+ * not only a number). */
 const char *moe_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

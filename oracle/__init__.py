@@ -43,6 +43,8 @@ def _load():
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
     lib.oracle_bf16_round.restype = ctypes.c_uint16
     lib.oracle_bf16_round_array.argtypes = [vp, i64, vp]
+    lib.oracle_threads.argtypes = [i32]
+    lib.oracle_threads.restype = i32
     lib.oracle_init()
     _lib = lib
     return lib
@@ -117,6 +119,12 @@ def route(logits, k):
     if rc:
         raise ValueError("oracle_route: invalid k=%d for E=%d" % (k, E))
     return idx, w
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops (n <= 0: unchanged); returns the
+    count in force.  Results do not depend on it."""
+    return int(_load().oracle_threads(int(n)))
 
 
 def silu(z: float) -> float:

@@ -69,6 +69,22 @@ static void build_tables(void) {
 
 int oracle_init(void) { build_tables(); return 0; }
 
+/* Threads of the parallel loops that follow (n <= 0: leave as is); returns
+ * the count now in force.  Only splits independent outputs: no result
+ * depends on it. */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 void oracle_tables(double *e2m1, double *e2m3, double *e4m3, double *ue8m0) {
     build_tables();
     memcpy(e2m1, T_E2M1, sizeof T_E2M1);

@@ -39,6 +39,11 @@ def _err(lib):
     return lib.moe_last_error().decode()
 
 
+def _ws_bytes(lib, L, T):
+    """moe_layer_workspace_bytes: the size, or 0 when the arguments break a rule."""
+    return lib.moe_layer_workspace_bytes(ctypes.byref(L), T)
+
+
 def _layer(**kw):
     d = dict(fmt=1, hidden=256, inter=512, n_experts=8, top_k=2, shared_inter=0,
              w13_codes=FAKE, w13_scales=FAKE, w2_codes=FAKE, w2_scales=FAKE)
@@ -68,32 +73,28 @@ def test_route_validation(lib):
 ])
 def test_layer_validation(lib, field, value, needle):
     L = _layer(**{field: value})
-    n = ctypes.c_size_t(0)
-    rc = lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n))
-    assert rc == moeq.MOE_EINVAL and needle in _err(lib)
-    assert n.value == 0
+    assert _ws_bytes(lib, L, 1) == 0 and needle in _err(lib)
 
 
 def test_e2m3_dims_must_be_whole_blocks(lib):
     L = _layer(fmt=2, hidden=256, inter=512 + 32)
-    n = ctypes.c_size_t(0)
-    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_EINVAL
+    assert _ws_bytes(lib, L, 1) == 0
     assert "multiple of 128" in _err(lib)
 
 
 def test_shared_pointers_required(lib):
     L = _layer(shared_inter=512)
-    n = ctypes.c_size_t(0)
-    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_EINVAL
+    assert _ws_bytes(lib, L, 1) == 0
     assert "sh13_codes" in _err(lib)
 
 
 def test_workspace_bytes_and_checks(lib):
     L = _layer()
-    n = ctypes.c_size_t(0)
-    assert lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n)) == moeq.MOE_OK
-    need = n.value
-    assert need > 16384
+    need = _ws_bytes(lib, L, 1)
+    assert need > 16384 and _err(lib) == ""
+    assert _ws_bytes(lib, L, 0) == 0 and "T=0" in _err(lib)
+    assert _ws_bytes(lib, L, 65537) == 0
+    assert lib.moe_layer_workspace_bytes(None, 1) == 0 and "NULL" in _err(lib)
     # too small, misaligned, NULL: workspace errors, nothing launched
     assert lib.moe_layer_decode(ctypes.byref(L), FAKE, FAKE, 1, FAKE, None, None, 0, FAKE2, need - 1,
                                 None) == moeq.MOE_EWORKSPACE
@@ -113,11 +114,10 @@ def test_many_token_workspace(lib):
     """T > 16 takes the many-token path: its workspace grows with the chunk
     (at most 2,048 tokens) and a smaller workspace is refused."""
     L = _layer()
-    n = ctypes.c_size_t(0)
     sizes = {}
     for T in (16, 17, 2048, 2049, 65536):
-        assert lib.moe_layer_workspace_bytes(ctypes.byref(L), T, ctypes.byref(n)) == moeq.MOE_OK
-        sizes[T] = n.value
+        sizes[T] = _ws_bytes(lib, L, T)
+        assert sizes[T] > 0
     assert sizes[17] < sizes[2048] == sizes[2049] == sizes[65536]
     H, I, k = L.hidden, max(L.inter, L.shared_inter), L.top_k
     assert sizes[2048] >= 2048 * (k + 1) * (H * 4 + I * 4)      # fp32 partials + h pair per (token, expert)
@@ -128,12 +128,11 @@ def test_many_token_workspace(lib):
 
 def test_expert_ffn_validation(lib):
     L = _layer()
-    n = ctypes.c_size_t(0)
-    lib.moe_layer_workspace_bytes(ctypes.byref(L), 1, ctypes.byref(n))
-    assert lib.moe_expert_ffn_q(ctypes.byref(L), 8, FAKE, 1, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
-    assert lib.moe_expert_ffn_q(ctypes.byref(L), -1, FAKE, 1, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
+    n = _ws_bytes(lib, L, 1)
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), 8, FAKE, 1, FAKE, 0, FAKE2, n, None) == moeq.MOE_EINVAL
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), -1, FAKE, 1, FAKE, 0, FAKE2, n, None) == moeq.MOE_EINVAL
     assert "shared" in _err(lib)
-    assert lib.moe_expert_ffn_q(ctypes.byref(L), 0, FAKE, 0, FAKE, 0, FAKE2, n.value, None) == moeq.MOE_EINVAL
+    assert lib.moe_expert_ffn_q(ctypes.byref(L), 0, FAKE, 0, FAKE, 0, FAKE2, n, None) == moeq.MOE_EINVAL
 
 
 def test_gemv_validation(lib):
