@@ -6,8 +6,8 @@ libmoeq.so.  There is no fallback: if the library is not built, or a tensor is
 not on the GPU, the call raises.
 
 Functions carry the C names: moe_route_topk, moe_layer_workspace_bytes,
-moe_expert_ffn_q, moe_layer_decode, dense_gemv_q, moe_workspace_status,
-moe_last_error, moe_version.
+moe_expert_ffn_q, moe_layer_decode, moe_layer_decode_noalloc, dense_gemv_q,
+moe_workspace_status, moe_last_error, moe_version.
 """
 import ctypes
 import os
@@ -63,12 +63,14 @@ def load_library(path=None):
     lib.moe_layer_workspace_bytes.restype = sz
     lib.moe_expert_ffn_q.argtypes = [ctypes.POINTER(moe_layer), i32, vp, i32, vp, i32, vp, sz, vp]
     lib.moe_layer_decode.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.moe_layer_decode_noalloc.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp]
     lib.dense_gemv_q.argtypes = [ctypes.POINTER(moe_qmat), vp, i32, vp, i32, vp]
     lib.moe_workspace_status.argtypes = [vp, sz, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_version.restype = i32
-    for f in ("moe_route_topk", "moe_expert_ffn_q", "moe_layer_decode", "dense_gemv_q", "moe_workspace_status"):
+    for f in ("moe_route_topk", "moe_expert_ffn_q", "moe_layer_decode", "moe_layer_decode_noalloc", "dense_gemv_q",
+              "moe_workspace_status"):
         getattr(lib, f).restype = i32
     if path is None:
         _lib = lib
@@ -248,6 +250,26 @@ def moe_layer_decode(layer, x, logits, out=None, idx_out=None, w_out=None, flags
                                            _dev(logits, "logits", (torch.float32,)), T,
                                            _dev(out, "out", (torch.bfloat16, torch.float32)), pi, pw, flags,
                                            _dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return out
+
+
+def moe_layer_decode_noalloc(layer, x, logits, out, idx_out=None, w_out=None, flags=0):
+    """moe_layer_decode on the library's static workspace (T <= 16): the caller
+    passes every output, nothing is allocated."""
+    T = x.shape[0]
+    _shape(x, "x", (T, layer.hidden))
+    _shape(logits, "logits", (T, layer.n_experts))
+    _shape(out, "out", (T, layer.hidden))
+    if idx_out is not None:
+        _shape(idx_out, "idx_out", (T, layer.top_k))
+    if w_out is not None:
+        _shape(w_out, "w_out", (T, layer.top_k))
+    pi = _dev(idx_out, "idx_out", (torch.int32,)) if idx_out is not None else None
+    pw = _dev(w_out, "w_out", (torch.float32,)) if w_out is not None else None
+    _check(load_library().moe_layer_decode_noalloc(ctypes.byref(layer.c), _dev(x, "x", _BF16),
+                                                   _dev(logits, "logits", (torch.float32,)), T,
+                                                   _dev(out, "out", (torch.bfloat16, torch.float32)), pi, pw, flags,
+                                                   _stream()))
     return out
 
 

@@ -14,6 +14,7 @@
 
 using namespace moeq;
 
+static_assert(NOALLOC_SCRATCH_BYTES == MOE_NOALLOC_WORKSPACE_BYTES, "static workspace size");
 
 static thread_local char g_err[512];
 
@@ -231,6 +232,45 @@ int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
     hipError_t e = launch_layer(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_layer_decode launch", e);
+    return ok();
+}
+
+int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *logits, int T, void *out,
+                             int32_t *idx_out, float *w_out, int flags, void *stream) {
+    CHECK(validate_layer(L));
+    if (T < 1 || T > DEC_MAX_T)
+        return fail(MOE_EINVAL, "T=%d must be in [1, %d] (the static workspace serves the decode path only)", T,
+                    DEC_MAX_T);
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("logits", logits));
+    CHECK(check_ptr("out", out));
+    if (idx_out && !al16(idx_out)) return fail(MOE_EINVAL, "idx_out is not 16-byte aligned");
+    if (w_out && !al16(w_out)) return fail(MOE_EINVAL, "w_out is not 16-byte aligned");
+    CHECK(decode_supported(L, T));
+    const size_t need = ws_need(L, T);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_EWORKSPACE, "this layer needs %zu bytes of workspace; the static workspace holds %zu", need,
+                    (size_t)NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    const char *why = "";
+    hipError_t e = noalloc_workspace((hipStream_t)stream, &ws, &why);
+    if (e != hipSuccess) return fail(MOE_EHIP, "static workspace set-up: %s (%s)", why, hipGetErrorString(e));
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.L = layer_args(L);
+    a.x = (const uint16_t *)x;
+    a.logits = logits;
+    a.T = T;
+    a.out = out;
+    a.idx_out = idx_out;
+    a.w_out = w_out;
+    a.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+    a.mode = MODE_ROUTE;
+    a.fixed_e = 0;
+    a.ws = (uint8_t *)ws;
+    a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_layer_decode_noalloc launch", e);
     return ok();
 }
 

@@ -74,6 +74,14 @@ hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s);
 
 int decoder_choice();    // DEC_LUT or DEC_HW (MOEQ_DECODER=lut|hw, read once)
 
+// The library-owned workspace of moe_layer_decode_noalloc (noalloc.hip): a
+// static device array per GPU.  noalloc_workspace gives its address on the
+// current device (cleared on the first call there, which must not be under
+// graph capture).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+hipError_t noalloc_workspace(hipStream_t s, void **ptr, const char **why);
+
 // Cached runtime queries (launch_cache.cpp), per device; thread-safe.
 int current_device();
 int cached_cus();                                                  // CUs of the current device

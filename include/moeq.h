@@ -182,6 +182,25 @@ int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int
                      int32_t *idx_out, float *w_out, int flags, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* moe_layer_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results as moe_layer_decode, with a workspace the library owns
+ * instead of the caller's.  That workspace is one static device array of
+ * MOE_NOALLOC_WORKSPACE_BYTES per GPU, held from the library's load until the
+ * process ends; the call allocates nothing.  Limits: 1 <= T <= 16 (the decode
+ * kernels) and moe_layer_workspace_bytes(L, T) <= MOE_NOALLOC_WORKSPACE_BYTES,
+ * else MOE_EINVAL / MOE_EWORKSPACE.  The first call on a device clears the
+ * array (a fill kernel on `stream`) and must not be made under graph capture
+ * (MOE_EHIP names the reason); later calls may be captured.  Every call on a
+ * GPU shares its array, which keeps the previous call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  An expired in-kernel wait leaves the output
+ * invalid and is not reported here (moe_workspace_status needs a caller
+ * workspace). */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *logits, int T, void *out,
+                             int32_t *idx_out, float *w_out, int flags, void *stream);
+
 /* Dense block-scaled GEMV: y[b] = W x[b] for B tokens sharing every decoded
  * weight (knivesysl README, "formats": the fp6 projections).
  *   x: device bf16 [B][cols];  y: device [B][rows], bf16 or fp32 (MOE_OUT_F32)
