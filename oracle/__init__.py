@@ -13,8 +13,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
 _lib = None
 
-FMT_E2M1 = 1
-FMT_E2M3 = 2
+FMT_E2M1 = 1          # e2m1 + e4m3 per 16
+FMT_E2M3 = 2          # e2m3 + UE8M0 per 128
+FMT_MXFP4 = 3         # e2m1 + UE8M0 per 32
+FMT_INT4_F16 = 4      # int4 + fp16 per 64
+FMT_E2M3_E4M3 = 5     # e2m3 + e4m3 per 16
+FORMATS = (FMT_E2M1, FMT_E2M3, FMT_MXFP4, FMT_INT4_F16, FMT_E2M3_E4M3)
 
 
 def _load():
@@ -43,6 +47,13 @@ def _load():
     lib.oracle_bf16_round.argtypes = [ctypes.c_double]
     lib.oracle_bf16_round.restype = ctypes.c_uint16
     lib.oracle_bf16_round_array.argtypes = [vp, i64, vp]
+    lib.oracle_fp16_value.argtypes = [ctypes.c_uint]
+    lib.oracle_fp16_value.restype = ctypes.c_double
+    lib.oracle_int4_table.argtypes = [vp]
+    lib.oracle_code_row_bytes.argtypes = [i32, i64]
+    lib.oracle_code_row_bytes.restype = i64
+    lib.oracle_scale_row_bytes.argtypes = [i32, i64]
+    lib.oracle_scale_row_bytes.restype = i64
     lib.oracle_threads.argtypes = [i32]
     lib.oracle_threads.restype = i32
     lib.oracle_init()
@@ -56,19 +67,25 @@ def _c(a, dtype):
 
 
 def code_row_bytes(fmt, cols):
-    return cols // 2 if fmt == FMT_E2M1 else cols * 3 // 4
+    return int(_load().oracle_code_row_bytes(fmt, cols))
 
 
 def scale_row_bytes(fmt, cols):
-    return cols // 16 if fmt == FMT_E2M1 else cols // 128
+    return int(_load().oracle_scale_row_bytes(fmt, cols))
 
 
 def tables():
-    """The four decode tables: e2m1[16], e2m3[64], e4m3[256], ue8m0[256]."""
+    """The decode tables: e2m1[16], e2m3[64], e4m3[256], ue8m0[256], int4[16]."""
     lib = _load()
-    t = [np.empty(n, np.float64) for n in (16, 64, 256, 256)]
-    lib.oracle_tables(*[a.ctypes.data for a in t])
-    return {"e2m1": t[0], "e2m3": t[1], "e4m3": t[2], "ue8m0": t[3]}
+    t = [np.empty(n, np.float64) for n in (16, 64, 256, 256, 16)]
+    lib.oracle_tables(*[a.ctypes.data for a in t[:4]])
+    lib.oracle_int4_table(t[4].ctypes.data)
+    return {"e2m1": t[0], "e2m3": t[1], "e4m3": t[2], "ue8m0": t[3], "int4": t[4]}
+
+
+def fp16_value(bits: int) -> float:
+    """The IEEE binary16 value of a 16-bit pattern (the int4 format's group scale)."""
+    return float(_load().oracle_fp16_value(int(bits)))
 
 
 def bf16_value(bits: int) -> float:

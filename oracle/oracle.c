@@ -30,13 +30,19 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_FMT_E2M1 1   /* e2m1 codes, fp8 e4m3 scale per 16 weights */
-#define ORACLE_FMT_E2M3 2   /* e2m3 codes, UE8M0 (power of two) scale per 128 weights */
+#define ORACLE_FMT_E2M1 1        /* e2m1 codes, fp8 e4m3 scale per 16 weights */
+#define ORACLE_FMT_E2M3 2        /* e2m3 codes, UE8M0 (power of two) scale per 128 weights */
+#define ORACLE_FMT_MXFP4 3       /* e2m1 codes, UE8M0 scale per 32 weights (colibri README, model
+                                    notes: Kimi K3's MXFP4 experts) */
+#define ORACLE_FMT_INT4_F16 4    /* int4 codes, fp16 scale per 64 weights (colibri README, "Get the
+                                    model": the group-scaled gs64 int4 container) */
+#define ORACLE_FMT_E2M3_E4M3 5   /* e2m3 codes, fp8 e4m3 scale per 16 weights */
 
 static double T_E2M1[16];
 static double T_E2M3[64];
 static double T_E4M3[256];
 static double T_UE8M0[256];
+static double T_INT4[16];
 static int tables_ready = 0;
 
 /* A minifloat with one sign bit, ebits exponent bits of bias `bias`, mbits
@@ -64,7 +70,28 @@ static void build_tables(void) {
         /* UE8M0: unsigned, eight exponent bits, bias 127, no mantissa; 0xFF is NaN */
         T_UE8M0[b] = (b == 0xFF) ? NAN : ldexp(1.0, (int)b - 127);
     }
+    /* int4: the code read as a two's-complement 4-bit integer (bit 3 weighs -8) */
+    for (unsigned c = 0; c < 16; ++c) T_INT4[c] = (double)(c & 7u) - ((c & 8u) ? 8.0 : 0.0);
     tables_ready = 1;
+}
+
+/* IEEE 754 binary16 from its bit fields: sign bit 15, five exponent bits of
+ * bias 15, ten mantissa bits.  Exponent field 0: subnormal (m / 2^10) * 2^-14;
+ * field 31: infinity (m == 0) or NaN. */
+static double fp16_value(unsigned h) {
+    unsigned s = (h >> 15) & 1u, e = (h >> 10) & 31u, m = h & 1023u;
+    double mag;
+    if (e == 31) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)m / 1024.0, -14);
+    else mag = ldexp(1.0 + (double)m / 1024.0, (int)e - 15);
+    return s ? -mag : mag;
+}
+
+double oracle_fp16_value(unsigned h) { return fp16_value(h); }
+
+void oracle_int4_table(double *int4) {
+    build_tables();
+    memcpy(int4, T_INT4, sizeof T_INT4);
 }
 
 int oracle_init(void) { build_tables(); return 0; }
@@ -103,12 +130,25 @@ static double bf16_value(uint16_t h) {
 
 double oracle_bf16_value(uint16_t h) { return bf16_value(h); }
 
-int64_t oracle_code_row_bytes(int fmt, int64_t cols) { return fmt == ORACLE_FMT_E2M1 ? cols / 2 : cols * 3 / 4; }
-int64_t oracle_scale_row_bytes(int fmt, int64_t cols) { return fmt == ORACLE_FMT_E2M1 ? cols / 16 : cols / 128; }
+/* Formats whose codes are four bits wide (two per byte); the others are six. */
+static int four_bit(int fmt) { return fmt == ORACLE_FMT_E2M1 || fmt == ORACLE_FMT_MXFP4 || fmt == ORACLE_FMT_INT4_F16; }
+
+int64_t oracle_code_row_bytes(int fmt, int64_t cols) { return four_bit(fmt) ? cols / 2 : cols * 3 / 4; }
+
+/* Scale bytes per row: one byte per block of 16 (e4m3), 32 or 128 (UE8M0)
+ * weights; two bytes (little-endian fp16) per group of 64 for int4. */
+int64_t oracle_scale_row_bytes(int fmt, int64_t cols) {
+    switch (fmt) {
+        case ORACLE_FMT_E2M1: case ORACLE_FMT_E2M3_E4M3: return cols / 16;
+        case ORACLE_FMT_E2M3: return cols / 128;
+        case ORACLE_FMT_MXFP4: return cols / 32;
+        default: return 2 * (cols / 64);
+    }
+}
 
 /* The code of element j in one packed row. */
 static unsigned code_at(int fmt, const uint8_t *row, int64_t j) {
-    if (fmt == ORACLE_FMT_E2M1) {
+    if (four_bit(fmt)) {
         uint8_t b = row[j >> 1];
         return (j & 1) ? (b >> 4) : (b & 0x0F);          /* low nibble holds the even element */
     }
@@ -123,8 +163,17 @@ static unsigned code_at(int fmt, const uint8_t *row, int64_t j) {
 
 /* W[j] of one row: the code's value times its block's scale (exact in double). */
 static double weight_at(int fmt, const uint8_t *crow, const uint8_t *srow, int64_t j) {
-    if (fmt == ORACLE_FMT_E2M1) return T_E2M1[code_at(fmt, crow, j)] * T_E4M3[srow[j / 16]];
-    return T_E2M3[code_at(fmt, crow, j)] * T_UE8M0[srow[j / 128]];
+    const unsigned c = code_at(fmt, crow, j);
+    switch (fmt) {
+        case ORACLE_FMT_E2M1: return T_E2M1[c] * T_E4M3[srow[j / 16]];
+        case ORACLE_FMT_E2M3: return T_E2M3[c] * T_UE8M0[srow[j / 128]];
+        case ORACLE_FMT_MXFP4: return T_E2M1[c] * T_UE8M0[srow[j / 32]];
+        case ORACLE_FMT_E2M3_E4M3: return T_E2M3[c] * T_E4M3[srow[j / 16]];
+        default: {   /* int4: the group's fp16 scale, low byte first */
+            const uint8_t *g = srow + 2 * (j / 64);
+            return T_INT4[c] * fp16_value((unsigned)g[0] | ((unsigned)g[1] << 8));
+        }
+    }
 }
 
 /* Decode a whole matrix [rows][cols] to double. */

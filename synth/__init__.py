@@ -10,6 +10,9 @@ Layouts produced (row-major, each row contiguous, planar codes and scales):
   e2m3  codes [rows][3*cols/4] (element j in bits [6j, 6j+6) of the row's
         little-endian bit string)
         scales [rows][cols/128] (UE8M0, one per 128 consecutive weights)
+  MXFP4 (e2m1 + UE8M0/32) and int4 (+ fp16/64) codes as e2m1; e2m3 + e4m3/16
+        codes as e2m3; scales [rows][cols/32] (one byte), [rows][cols/64][2]
+        (fp16, low byte first), [rows][cols/16] (e4m3).
 Uniform random code bytes make every 4-bit or 6-bit code uniform.
 """
 import ctypes
@@ -18,7 +21,7 @@ import os
 import numpy as np
 
 from . import configs
-from .configs import FMT_E2M1, FMT_E2M3, GemvConfig, MoEConfig
+from .configs import FMT_E2M1, FMT_E2M3, FMT_E2M3_E4M3, FMT_INT4_F16, FMT_MXFP4, FORMATS, GemvConfig, MoEConfig
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_build", "libsynth.so")
@@ -52,6 +55,9 @@ def _load():
     lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, d, vp]
     lib.synth_bf16_from_double.argtypes = [d]
     lib.synth_bf16_from_double.restype = ctypes.c_uint16
+    lib.synth_fp16_loguniform.argtypes = [u64, u64, u64, u64, d, d, vp]
+    lib.synth_fp16_encode.argtypes = [d]
+    lib.synth_fp16_encode.restype = ctypes.c_uint16
     lib.synth_e4m3_encode.argtypes = [d]
     lib.synth_e4m3_encode.restype = ctypes.c_uint8
     _lib = lib
@@ -82,6 +88,17 @@ def ue8m0_uniform(seed, stream, n, lo, hi, offset=0, out=None):
     return out
 
 
+def fp16_loguniform(seed, stream, n, lo, hi, offset=0, out=None):
+    """n fp16 scales (2n bytes, low byte first) of values 2^U[lo, hi)."""
+    out = np.empty(2 * n, np.uint8) if out is None else out
+    _load().synth_fp16_loguniform(seed, stream, offset, n, lo, hi, _ptr(out))
+    return out
+
+
+def fp16_encode(v: float) -> int:
+    return int(_load().synth_fp16_encode(float(v)))
+
+
 def normal_bf16(seed, stream, n, sigma=1.0, offset=0, out=None):
     out = np.empty(n, np.uint16) if out is None else out
     _load().synth_normal_bf16(seed, stream, offset, n, sigma, _ptr(out))
@@ -104,22 +121,25 @@ def e4m3_encode(v: float) -> int:
 
 # ---------------------------------------------------------------- layouts
 def code_row_bytes(fmt: int, cols: int) -> int:
-    return cols // 2 if fmt == FMT_E2M1 else cols * 3 // 4
+    return cols // 2 if fmt in (FMT_E2M1, FMT_MXFP4, FMT_INT4_F16) else cols * 3 // 4
 
 
 def scale_row_bytes(fmt: int, cols: int) -> int:
-    return cols // 16 if fmt == FMT_E2M1 else cols // 128
+    return {FMT_E2M1: cols // 16, FMT_E2M3: cols // 128, FMT_MXFP4: cols // 32, FMT_INT4_F16: cols // 32,
+            FMT_E2M3_E4M3: cols // 16}[fmt]
 
 
 def fill_matrix(fmt, rows, cols, seed, codes_stream, scales_stream, codes_out, scales_out,
-                scale_log2=(-6.0, -2.0), ue8m0_exp=(-8, -3)):
+                scale_log2=(-6.0, -2.0), ue8m0_exp=(-8, -3), fp16_log2=(-8.0, -4.0)):
     """Draw one block-scaled matrix [rows][cols] into flat uint8 views."""
     nc = rows * code_row_bytes(fmt, cols)
     ns = rows * scale_row_bytes(fmt, cols)
     assert codes_out.size == nc and scales_out.size == ns
     random_bytes(seed, codes_stream, nc, out=codes_out)
-    if fmt == FMT_E2M1:
+    if fmt in (FMT_E2M1, FMT_E2M3_E4M3):
         e4m3_loguniform(seed, scales_stream, ns, scale_log2[0], scale_log2[1], out=scales_out)
+    elif fmt == FMT_INT4_F16:
+        fp16_loguniform(seed, scales_stream, ns // 2, fp16_log2[0], fp16_log2[1], out=scales_out)
     else:
         ue8m0_uniform(seed, scales_stream, ns, ue8m0_exp[0], ue8m0_exp[1], out=scales_out)
 
@@ -145,7 +165,7 @@ def fill_expert(cfg: MoEConfig, e: int, out: dict):
     """Expert e's four arrays (e == cfg.experts is the shared expert) into `out`
     (dict of flat or shaped uint8 arrays with the sizes of expert_shapes)."""
     I = cfg.shared_inter if e == cfg.experts else cfg.inter
-    kw = dict(scale_log2=cfg.scale_log2, ue8m0_exp=cfg.ue8m0_exp)
+    kw = dict(scale_log2=cfg.scale_log2, ue8m0_exp=cfg.ue8m0_exp, fp16_log2=cfg.fp16_log2)
     fill_matrix(cfg.fmt, 2 * I, cfg.hidden, cfg.seed, stream_id(K_W13_CODES, e), stream_id(K_W13_SCALES, e),
                 out["w13_codes"].reshape(-1), out["w13_scales"].reshape(-1), **kw)
     fill_matrix(cfg.fmt, cfg.hidden, I, cfg.seed, stream_id(K_W2_CODES, e), stream_id(K_W2_SCALES, e),
@@ -185,11 +205,12 @@ def router_logits(cfg, tokens=None, sub=0) -> np.ndarray:
 # ---------------------------------------------------------------- dense GEMV
 def gemv_weights(cfg: GemvConfig):
     return matrix(cfg.fmt, cfg.rows, cfg.cols, cfg.seed, stream_id(K_W_CODES, 0), stream_id(K_W_SCALES, 0),
-                  scale_log2=cfg.scale_log2, ue8m0_exp=cfg.ue8m0_exp)
+                  scale_log2=cfg.scale_log2, ue8m0_exp=cfg.ue8m0_exp, fp16_log2=cfg.fp16_log2)
 
 
 def gemv_x(cfg: GemvConfig, batch: int, sub=0) -> np.ndarray:
     return normal_bf16(cfg.seed, stream_id(K_X, sub), batch * cfg.cols, cfg.x_sigma).reshape(batch, cfg.cols)
 
 
-__all__ = ["configs", "FMT_E2M1", "FMT_E2M3", "MoEConfig", "GemvConfig"]
+__all__ = ["configs", "FMT_E2M1", "FMT_E2M3", "FMT_MXFP4", "FMT_INT4_F16", "FMT_E2M3_E4M3", "FORMATS", "MoEConfig",
+           "GemvConfig"]

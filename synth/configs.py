@@ -9,8 +9,12 @@ top-8 layer, 2,048-token prompt chunks and a 5120-wide dense model.
 from dataclasses import dataclass, field
 from typing import Optional, Tuple
 
-FMT_E2M1 = 1   # 4-bit e2m1 codes, one fp8-e4m3 scale per 16 weights
-FMT_E2M3 = 2   # 6-bit e2m3 codes, one power-of-two (UE8M0) scale per 128 weights
+FMT_E2M1 = 1        # 4-bit e2m1 codes, one fp8-e4m3 scale per 16 weights
+FMT_E2M3 = 2        # 6-bit e2m3 codes, one power-of-two (UE8M0) scale per 128 weights
+FMT_MXFP4 = 3       # 4-bit e2m1 codes, one UE8M0 scale per 32 weights
+FMT_INT4_F16 = 4    # 4-bit two's-complement integers, one fp16 scale per 64 weights
+FMT_E2M3_E4M3 = 5   # 6-bit e2m3 codes, one fp8-e4m3 scale per 16 weights
+FORMATS = (FMT_E2M1, FMT_E2M3, FMT_MXFP4, FMT_INT4_F16, FMT_E2M3_E4M3)
 
 
 @dataclass(frozen=True)
@@ -26,7 +30,8 @@ class MoEConfig:
     logit_sigma: float = 1.0         # router logits ~ N(0, sigma), fp32
     x_sigma: float = 1.0             # hidden state ~ N(0, sigma), rounded to bf16
     scale_log2: Tuple[float, float] = (-6.0, -2.0)   # e4m3 scales: 2^U[lo, hi)
-    ue8m0_exp: Tuple[int, int] = (-8, -3)           # e2m3 scales: 2^e, e uniform integer
+    ue8m0_exp: Tuple[int, int] = (-8, -3)           # UE8M0 scales: 2^e, e uniform integer
+    fp16_log2: Tuple[float, float] = (-8.0, -4.0)   # fp16 scales (int4): 2^U[lo, hi)
     seed: int = 0
     description: str = ""
 
@@ -40,6 +45,7 @@ class GemvConfig:
     fmt: int = FMT_E2M3
     ue8m0_exp: Tuple[int, int] = (-8, -3)
     scale_log2: Tuple[float, float] = (-6.0, -2.0)
+    fp16_log2: Tuple[float, float] = (-8.0, -4.0)
     x_sigma: float = 1.0
     seed: int = 0
     description: str = ""

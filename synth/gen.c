@@ -90,6 +90,32 @@ void synth_ue8m0_uniform(uint64_t seed, uint64_t stream, uint64_t offset, uint64
     }
 }
 
+/* Round a double in fp16's positive normal range [2^-14, 65504] to the nearest
+ * IEEE binary16 (ten mantissa bits), ties to even.  Returns the bit pattern. */
+static uint16_t fp16_encode_pos_normal(double v) {
+    int e;
+    double f = frexp(v, &e);                  /* v = f * 2^e, f in [0.5, 1) */
+    double r = nearbyint(ldexp(f, 11));       /* 11 significant bits: 1024..2048 */
+    if (r == 2048.0) { r = 1024.0; e += 1; }
+    return (uint16_t)(((e - 1 + 15) << 10) | (int)(r - 1024.0));
+}
+
+/* fp16 group scales 2^u, u ~ U[lo, hi), rounded to binary16, stored as two
+ * bytes each, low byte first (lo and hi keep the values normal). */
+void synth_fp16_loguniform(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t n,
+                           double lo, double hi, uint8_t *out) {
+    const uint64_t key = stream_key(seed, stream);
+    #pragma omp parallel for schedule(static) if (n > (1u << 18))
+    for (int64_t i = 0; i < (int64_t)n; ++i) {
+        double u = lo + (hi - lo) * unit53(word_at(key, offset + (uint64_t)i));
+        uint16_t h = fp16_encode_pos_normal(exp2(u));
+        out[2 * i] = (uint8_t)(h & 0xFF);
+        out[2 * i + 1] = (uint8_t)(h >> 8);
+    }
+}
+
+uint16_t synth_fp16_encode(double v) { return fp16_encode_pos_normal(v); }
+
 /* Standard normal by Box-Muller (cosine branch), one normal per counter, from
  * two 53-bit uniforms taken from words 2c and 2c+1. */
 static inline double normal_at(uint64_t key, uint64_t c) {

@@ -30,6 +30,19 @@ def read_packing_examples():
     return rows
 
 
+def read_format_variants():
+    """Rows of golden/format_variants.txt: (format name, code bytes, scale bytes, values)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "format_variants.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fmt, codes, scales, vals = [p.strip() for p in line.split("|")]
+            rows.append((fmt, bytes.fromhex(codes), bytes.fromhex(scales), [float(v) for v in vals.split()]))
+    return rows
+
+
 def max_rel_err(y, ref):
     """Max over elements of |y - ref| / max(|ref|, tau), tau = 1e-2 * max|ref|.
 

@@ -14,7 +14,7 @@ from scipy.special import expit, softmax
 
 import oracle
 import synth
-from helpers import read_packing_examples, read_table
+from helpers import read_format_variants, read_packing_examples, read_table
 from synth.configs import MoEConfig
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
@@ -28,7 +28,19 @@ MUTANTS = {
                       "ldexp((double)m / (double)(1u << mbits), -bias)"),
     "nibble_order": ("(j & 1) ? (b >> 4) : (b & 0x0F)", "(j & 1) ? (b & 0x0F) : (b >> 4)"),
     "e2m3_bit_order": ("& 1) << t;", "& 1) << (5 - t);"),
-    "scale_block": ("srow[j / 16]", "srow[j / 32]"),
+    "scale_block": ("case ORACLE_FMT_E2M1: return T_E2M1[c] * T_E4M3[srow[j / 16]];",
+                    "case ORACLE_FMT_E2M1: return T_E2M1[c] * T_E4M3[srow[j / 32]];"),
+    "mxfp4_block": ("T_E2M1[c] * T_UE8M0[srow[j / 32]]", "T_E2M1[c] * T_UE8M0[srow[j / 16]]"),
+    "mxfp4_scale_kind": ("T_E2M1[c] * T_UE8M0[srow[j / 32]]", "T_E2M1[c] * T_E4M3[srow[j / 32]]"),
+    "mxfp4_six_bit": ("fmt == ORACLE_FMT_MXFP4 || ", ""),
+    "int4_unsigned": ("T_INT4[c] = (double)(c & 7u) - ((c & 8u) ? 8.0 : 0.0);", "T_INT4[c] = (double)c;"),
+    "int4_offset_binary": ("T_INT4[c] = (double)(c & 7u) - ((c & 8u) ? 8.0 : 0.0);", "T_INT4[c] = (double)c - 8.0;"),
+    "int4_group": ("srow + 2 * (j / 64)", "srow + 2 * (j / 32)"),
+    "fp16_byte_order": ("(unsigned)g[0] | ((unsigned)g[1] << 8)", "(unsigned)g[1] | ((unsigned)g[0] << 8)"),
+    "fp16_bias": ("ldexp(1.0 + (double)m / 1024.0, (int)e - 15)", "ldexp(1.0 + (double)m / 1024.0, (int)e - 16)"),
+    "fp16_subnormal": ("ldexp((double)m / 1024.0, -14)", "ldexp((double)m / 1024.0, -15)"),
+    "e2m3_e4m3_block": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_E4M3[srow[j / 128]]"),
+    "e2m3_e4m3_scale_kind": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_UE8M0[srow[j / 16]]"),
     "ue8m0_bias": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
     "bf16_widen": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
     "gemv_last_col": ("for (int64_t j = 0; j < cols; ++j) acc += weight_at(fmt, crow, srow, j) * bf16_value(x[j]);",
@@ -143,7 +155,46 @@ def _pin_ffn_and_layer():
     assert np.allclose(b[0] - a[0], ysh, rtol=1e-12, atol=1e-12 * np.abs(ysh).max())
 
 
-PINS = [_pin_tables, _pin_packing, _pin_scale_blocks, _pin_gemv, _pin_route, _pin_silu, _pin_ffn_and_layer]
+def _pin_formats():
+    """The further formats: int4 by sign extension, fp16 by numpy on a spread of
+    patterns, the hand-worked rows, and one block placement each."""
+    c = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(oracle.tables()["int4"], ((c << 4).astype(np.int8) >> 4).astype(np.float64))
+    for b in list(range(0, 1 << 16, 97)) + [0x0001, 0x03FF, 0x0400, 0x3C00, 0x3555, 0x7BFF, 0x8001]:
+        ref = float(np.array([b], np.uint16).view(np.float16)[0])
+        got = oracle.fp16_value(b)
+        assert (np.isnan(ref) and np.isnan(got)) or got == ref
+    names = {"mxfp4": 3, "int4": 4, "e2m3_e4m3": 5}
+    for name, row, srow, vals in read_format_variants():
+        fmt = names[name]
+        cols = 128
+        codes = np.zeros(oracle.code_row_bytes(fmt, cols), np.uint8)
+        codes[: len(row)] = np.frombuffer(row, np.uint8)
+        scales = np.frombuffer(srow * (oracle.scale_row_bytes(fmt, cols) // len(srow)), np.uint8).copy()
+        assert list(oracle.decode(fmt, 1, cols, codes, scales)[0][: len(vals)]) == vals
+    # block placement: value 1.0 everywhere, a distinct scale per block
+    for fmt, one_byte, block, sc in ((3, 0x22, 32, [120, 121, 122, 123]), (5, None, 16, list(range(0x30, 0x38))),
+                                     (4, 0x11, 64, [0x00, 0x3C, 0x00, 0x40])):
+        cols = 128
+        if one_byte is not None:
+            codes = np.full((1, cols // 2), one_byte, np.uint8)
+        else:   # e2m3 code 8 (1.0) in every 6-bit slot
+            w = sum(8 << (6 * q) for q in range(4))
+            codes = np.tile(np.array([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], np.uint8), (1, cols // 4))
+        scales = np.array([sc], np.uint8)
+        W = oracle.decode(fmt, 1, cols, codes, scales)[0]
+        if fmt == 3:
+            expect = np.repeat(2.0 ** (np.array(sc, np.float64) - 127), block)
+        elif fmt == 4:
+            expect = np.repeat(np.array(sc, np.uint8).view("<u2").view(np.float16).astype(np.float64), block)
+        else:
+            import torch
+            expect = np.repeat(torch.tensor(sc, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy(), block)
+        assert np.array_equal(W, expect)
+
+
+PINS = [_pin_tables, _pin_packing, _pin_scale_blocks, _pin_gemv, _pin_route, _pin_silu, _pin_ffn_and_layer,
+        _pin_formats]
 
 
 def _failures():

@@ -86,3 +86,16 @@ def test_layer_shapes():
     assert L["w2_codes"].shape == (8, 256, 256) and L["w2_scales"].shape == (8, 256, 32)
     e3 = synth.expert_weights(cfg, 3)
     assert np.array_equal(e3["w2_codes"], L["w2_codes"][3])
+
+
+def test_fp16_encoder_matches_numpy():
+    """The int4 format's fp16 scales: round to nearest even over normal values."""
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([2.0 ** rng.uniform(-14, 15, 4000), [1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65504.0,
+                                                              2.0 ** -14]])
+    for v in vals:
+        assert synth.fp16_encode(float(v)) == int(np.float16(v).view(np.uint16)), v
+    b = synth.fp16_loguniform(0, 9, 5000, -8.0, -4.0)
+    h = b.view("<u2").view(np.float16).astype(np.float64)
+    assert (h >= 2.0 ** -8 * (1 - 2 ** -11)).all() and (h <= 2.0 ** -4 * (1 + 2 ** -11)).all()
+    assert abs(np.log2(h).mean() + 6.0) < 0.1
