@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "_build", "libmoeq.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EKERNEL = 0, -1, -2, -3, -4, -5
 MOE_FMT_E2M1_E4M3_B16, MOE_FMT_E2M3_UE8M0_B128 = 1, 2
+MOE_FMT_E2M1_UE8M0_B32, MOE_FMT_INT4_F16_B64, MOE_FMT_E2M3_E4M3_B16 = 3, 4, 5
+FORMATS = (1, 2, 3, 4, 5)
 MOE_OUT_F32 = 1
 MOE_DECODER_LUT = 1 << 28
 MOE_DECODER_HW = 1 << 29
@@ -123,13 +125,13 @@ def _numel(t, name, n):
 
 
 def code_row_bytes(fmt, cols):
-    """Bytes of one row of codes of `cols` weights."""
-    return cols // 2 if fmt == MOE_FMT_E2M1_E4M3_B16 else cols * 3 // 4
+    """Bytes of one row of codes of `cols` weights (four- or six-bit codes)."""
+    return cols * 3 // 4 if fmt in (MOE_FMT_E2M3_UE8M0_B128, MOE_FMT_E2M3_E4M3_B16) else cols // 2
 
 
 def scale_row_bytes(fmt, cols):
     """Scale bytes of one row of `cols` weights."""
-    return cols // 16 if fmt == MOE_FMT_E2M1_E4M3_B16 else cols // 128
+    return {1: cols // 16, 2: cols // 128, 3: cols // 32, 4: 2 * (cols // 64), 5: cols // 16}[fmt]
 
 
 class QMat:

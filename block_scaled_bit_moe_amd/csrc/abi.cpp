@@ -33,7 +33,18 @@ static int ok() {
 
 static bool al16(const void *p) { return p && (((uintptr_t)p) & 15u) == 0; }
 
-static int block_of(int fmt) { return fmt == MOE_FMT_E2M1_E4M3_B16 ? 32 : 128; }
+static bool fmt_known(int fmt) { return fmt >= MOE_FMT_E2M1_E4M3_B16 && fmt <= MOE_FMT_E2M3_E4M3_B16; }
+
+// Dimensions must hold whole scale blocks and give 16-byte code rows.
+static int block_of(int fmt) {
+    switch (fmt) {
+        case MOE_FMT_E2M1_E4M3_B16: return 32;
+        case MOE_FMT_E2M3_UE8M0_B128: return 128;
+        case MOE_FMT_E2M1_UE8M0_B32: return 32;
+        case MOE_FMT_INT4_F16_B64: return 64;
+        default: return 64;   // e2m3 + e4m3/16: 3*cols/4 bytes per row is a multiple of 16
+    }
+}
 
 static int check_dim(const char *name, int v, int fmt) {
     const int b = block_of(fmt);
@@ -78,8 +89,7 @@ int moeq::decoder_choice() {
 
 static int validate_layer(const moe_layer *L) {
     if (!L) return fail(MOE_EINVAL, "layer descriptor is NULL");
-    if (L->fmt != MOE_FMT_E2M1_E4M3_B16 && L->fmt != MOE_FMT_E2M3_UE8M0_B128)
-        return fail(MOE_EINVAL, "layer fmt=%d is not a known format", L->fmt);
+    if (!fmt_known(L->fmt)) return fail(MOE_EINVAL, "layer fmt=%d is not a known format", L->fmt);
     CHECK(check_dim("hidden", L->hidden, L->fmt));
     CHECK(check_dim("inter", L->inter, L->fmt));
     if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS)
@@ -276,8 +286,7 @@ int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *log
 
 int dense_gemv_q(const moe_qmat *W, const void *x, int B, void *y, int flags, void *stream) {
     if (!W) return fail(MOE_EINVAL, "matrix descriptor is NULL");
-    if (W->fmt != MOE_FMT_E2M1_E4M3_B16 && W->fmt != MOE_FMT_E2M3_UE8M0_B128)
-        return fail(MOE_EINVAL, "matrix fmt=%d is not a known format", W->fmt);
+    if (!fmt_known(W->fmt)) return fail(MOE_EINVAL, "matrix fmt=%d is not a known format", W->fmt);
     if (W->reserved != 0) return fail(MOE_EINVAL, "matrix reserved field must be 0");
     if (W->rows < 1 || W->rows > (1 << 24)) return fail(MOE_EINVAL, "rows=%d must be in [1, %d]", W->rows, 1 << 24);
     CHECK(check_dim("cols", W->cols, W->fmt));

@@ -1,16 +1,22 @@
 // common.h -- device building blocks shared by the gfx950 kernels.
 //
-// Formats (knivesysl README, "formats"; colibri README, "DeepSeek V4"):
+// Formats (knivesysl README, "formats"; colibri README, "DeepSeek V4" and its
+// model notes):
 //   FMT 1: e2m1 codes, two per byte (low nibble = even element), one fp8 e4m3
 //          scale per 16 weights;
-//   FMT 2: e2m3 codes as a little-endian 6-bit stream, one UE8M0 scale per 128.
+//   FMT 2: e2m3 codes as a little-endian 6-bit stream, one UE8M0 scale per 128;
+//   FMT 3: e2m1 codes, one UE8M0 scale per 32 (MXFP4);
+//   FMT 4: two's-complement int4 codes (packed as e2m1), one fp16 scale per 64
+//          (two bytes, low byte first);
+//   FMT 5: e2m3 codes, one fp8 e4m3 scale per 16.
 // Everything here works on "units" of 32 consecutive weights of one row:
-//   e2m1: 16 code bytes + 2 scale bytes (blocks 2u and 2u+1)
-//   e2m3: 24 code bytes + the scale byte of block u/4
-// A unit decodes to 16 bf16x2 registers (exact: every e2m1/e2m3 value has at
-// most 4 significant bits) which v_dot2c_f32_bf16 multiplies with 16 bf16x2 of
-// the activation, accumulating in fp32; the block scale is applied once per
-// block with an fp32 FMA.
+//   four-bit codes: 16 code bytes; six-bit codes: 24 code bytes; plus the
+//   unit's scale bits (two e4m3 bytes for the per-16 formats, the byte of its
+//   UE8M0 block, or the fp16 of its int4 group).
+// A unit decodes to 16 bf16x2 registers (exact: every e2m1, e2m3 and int4
+// value has at most 4 significant bits) which v_dot2c_f32_bf16 multiplies with
+// 16 bf16x2 of the activation, accumulating in fp32; the block scale is
+// applied once per block with an fp32 FMA.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,23 +32,30 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(6))) u32 u32x6_t;
 typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32_t;
 
-constexpr int FMT_E2M1 = 1;
-constexpr int FMT_E2M3 = 2;
+constexpr int FMT_E2M1 = 1;     // e2m1 + e4m3 per 16
+constexpr int FMT_E2M3 = 2;     // e2m3 + UE8M0 per 128
+constexpr int FMT_MXFP4 = 3;    // e2m1 + UE8M0 per 32
+constexpr int FMT_INT4 = 4;     // int4 + fp16 per 64
+constexpr int FMT_E2M3S = 5;    // e2m3 + e4m3 per 16
 constexpr int WAVE = 64;
 
+// Scale kinds
+constexpr int SC_E4M3 = 0, SC_UE8M0 = 1, SC_FP16 = 2;
+// Code kinds
+constexpr int CODE_E2M1 = 0, CODE_E2M3 = 1, CODE_INT4 = 2;
 
-template <int FMT> struct Fmt;
-template <> struct Fmt<FMT_E2M1> {
-    static constexpr int UNIT_CODE_BYTES = 16;
-    static constexpr int BLOCK = 16;
-    __host__ __device__ static inline int64_t code_row_bytes(int64_t cols) { return cols / 2; }
-    __host__ __device__ static inline int64_t scale_row_bytes(int64_t cols) { return cols / 16; }
-};
-template <> struct Fmt<FMT_E2M3> {
-    static constexpr int UNIT_CODE_BYTES = 24;
-    static constexpr int BLOCK = 128;
-    __host__ __device__ static inline int64_t code_row_bytes(int64_t cols) { return cols * 3 / 4; }
-    __host__ __device__ static inline int64_t scale_row_bytes(int64_t cols) { return cols / 128; }
+template <int FMT> struct Fmt {
+    static_assert(FMT >= 1 && FMT <= 5, "format");
+    static constexpr int CODE = (FMT == FMT_E2M1 || FMT == FMT_MXFP4) ? CODE_E2M1 : (FMT == FMT_INT4 ? CODE_INT4 : CODE_E2M3);
+    static constexpr bool SIX = CODE == CODE_E2M3;                 // six-bit codes
+    static constexpr int UNIT_CODE_BYTES = SIX ? 24 : 16;
+    static constexpr int BLOCK = FMT == FMT_E2M3 ? 128 : FMT == FMT_MXFP4 ? 32 : FMT == FMT_INT4 ? 64 : 16;
+    static constexpr int SCALE = (FMT == FMT_E2M1 || FMT == FMT_E2M3S) ? SC_E4M3 : (FMT == FMT_INT4 ? SC_FP16 : SC_UE8M0);
+    static constexpr bool TWO_SCALES = BLOCK == 16;                // two blocks per unit
+    __host__ __device__ static inline int64_t code_row_bytes(int64_t cols) { return SIX ? cols * 3 / 4 : cols / 2; }
+    __host__ __device__ static inline int64_t scale_row_bytes(int64_t cols) {
+        return SCALE == SC_FP16 ? 2 * (cols / BLOCK) : cols / BLOCK;
+    }
 };
 
 // ----------------------------------------------------------------------------
@@ -72,41 +85,52 @@ struct Luts {
     float *scale;   // e4m3 or UE8M0
 };
 
-// Fill the tables (call by the whole block, then __syncthreads()).
+// Fill the tables (call by the whole block, then __syncthreads()).  The pair
+// table holds two decoded codes per entry (e2m1 and int4: one byte; e2m3:
+// twelve bits); the scale table the format's scale byte (fp16 scales are
+// converted arithmetically and need none).
 template <int FMT>
 __device__ inline void build_luts(const Luts &L, int tid, int nthreads, bool need_pair) {
-    if (FMT == FMT_E2M1) {
-        if (need_pair)
-            for (int b = tid; b < LUT_E2M1_PAIR; b += nthreads) {
-                u32 lo = bf16_bits_exact(minifloat_value(b & 15, 2, 1, 1));
-                u32 hi = bf16_bits_exact(minifloat_value(b >> 4, 2, 1, 1));
-                L.pair[b] = lo | (hi << 16);
-            }
-        for (int b = tid; b < LUT_SCALE; b += nthreads)
-            L.scale[b] = ((b & 0x7F) == 0x7F) ? __builtin_nanf("") : minifloat_value(b, 4, 3, 7);
-    } else {
-        if (need_pair)
+    using F = Fmt<FMT>;
+    if (need_pair) {
+        if constexpr (F::CODE == CODE_E2M3) {
             for (int p = tid; p < LUT_E2M3_PAIR; p += nthreads) {
                 u32 lo = bf16_bits_exact(minifloat_value(p & 63, 2, 3, 1));
                 u32 hi = bf16_bits_exact(minifloat_value(p >> 6, 2, 3, 1));
                 L.pair[p] = lo | (hi << 16);
             }
-        for (int b = tid; b < LUT_SCALE; b += nthreads)
-            L.scale[b] = (b == 255) ? __builtin_nanf("") : ldexpf(1.0f, b - 127);
+        } else {
+            for (int b = tid; b < LUT_E2M1_PAIR; b += nthreads) {
+                u32 lo, hi;
+                if constexpr (F::CODE == CODE_E2M1) {
+                    lo = bf16_bits_exact(minifloat_value(b & 15, 2, 1, 1));
+                    hi = bf16_bits_exact(minifloat_value(b >> 4, 2, 1, 1));
+                } else {   // int4: the nibble as a signed 4-bit integer
+                    lo = bf16_bits_exact((float)(((int)((u32)b << 28)) >> 28));
+                    hi = bf16_bits_exact((float)(((int)((u32)b << 24)) >> 28));
+                }
+                L.pair[b] = lo | (hi << 16);
+            }
+        }
+    }
+    for (int b = tid; b < LUT_SCALE; b += nthreads) {
+        if constexpr (F::SCALE == SC_E4M3) L.scale[b] = ((b & 0x7F) == 0x7F) ? __builtin_nanf("") : minifloat_value(b, 4, 3, 7);
+        else L.scale[b] = (b == 255) ? __builtin_nanf("") : ldexpf(1.0f, b - 127);
     }
 }
 
 // ----------------------------------------------------------------------------
 // Raw unit loads
-template <int FMT> struct Unit;
-template <> struct Unit<FMT_E2M1> {
+template <bool SIX> struct UnitCodes;
+template <> struct UnitCodes<false> {
     uint4 c;        // 16 code bytes = 32 weights
-    u32 s;          // two e4m3 scale bytes in bits 0..15
 };
-template <> struct Unit<FMT_E2M3> {
+template <> struct UnitCodes<true> {
     uint2 c0, c1, c2;   // 24 code bytes = 32 weights
-    u32 s;              // the UE8M0 scale byte of this unit's block
 };
+// s: the unit's scale bits -- two e4m3 bytes in bits 0..15 (per-16 formats),
+// its UE8M0 block's byte, or its int4 group's fp16 bits
+template <int FMT> struct Unit : UnitCodes<Fmt<FMT>::SIX> { u32 s; };
 
 __device__ inline uint4 ldg16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ inline uint2 ldg8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
@@ -114,24 +138,34 @@ __device__ inline uint2 ldg8(const uint8_t *p) { return *reinterpret_cast<const 
 // Load unit u of a row (codes/scales point at the row's first byte).
 template <int FMT>
 __device__ inline void load_unit(Unit<FMT> &U, const uint8_t *codes, const uint8_t *scales, int u) {
-    if constexpr (FMT == FMT_E2M1) {
+    using F = Fmt<FMT>;
+    if constexpr (!F::SIX) {
         U.c = ldg16(codes + (int64_t)u * 16);
-        U.s = *reinterpret_cast<const uint16_t *>(scales + 2 * u);
     } else {
         const uint8_t *p = codes + (int64_t)u * 24;
         U.c0 = ldg8(p);
         U.c1 = ldg8(p + 8);
         U.c2 = ldg8(p + 16);
-        U.s = scales[u >> 2];
     }
+    if constexpr (F::TWO_SCALES) U.s = *reinterpret_cast<const uint16_t *>(scales + 2 * u);
+    else if constexpr (F::SCALE == SC_FP16) U.s = *reinterpret_cast<const uint16_t *>(scales + 2 * (u >> 1));
+    else U.s = scales[u / (F::BLOCK / 32)];
+}
+
+// int4 pair from a nibble pair: both nibbles sign-extended, converted exactly
+__device__ inline u32 int4_pair_bf16(u32 d, int shift) {
+    const int lo = ((int)(d << (28 - shift))) >> 28, hi = ((int)(d << (24 - shift))) >> 28;
+    const bf16x2_t b = bf16x2_t{(__bf16)(float)lo, (__bf16)(float)hi};
+    return __builtin_bit_cast(u32, b);
 }
 
 // Decode a unit into 16 bf16x2 words (pair i = weights 2i, 2i+1; low half = even).
 template <int FMT, int DEC>
 __device__ inline void decode_unit(const Unit<FMT> &U, const Luts &L, u32 w[16]) {
-    if constexpr (FMT == FMT_E2M1) {
+    using F = Fmt<FMT>;
+    if constexpr (!F::SIX) {
         const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
-        if constexpr (DEC == DEC_HW) {
+        if constexpr (DEC == DEC_HW && F::CODE == CODE_E2M1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 w[4 * i + 0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 0));
@@ -139,6 +173,11 @@ __device__ inline void decode_unit(const Unit<FMT> &U, const Luts &L, u32 w[16])
                 w[4 * i + 2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 2));
                 w[4 * i + 3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], 1.0f, 3));
             }
+        } else if constexpr (DEC == DEC_HW) {   // int4: sign extension and exact integer conversion
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) w[4 * i + b] = int4_pair_bf16(d[i], 8 * b);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -177,7 +216,7 @@ __device__ inline float dot2(u32 a, u32 b, float c) {
 // Two interleaved partial sums per block keep the dot2 dependency chains short.
 template <int FMT>
 __device__ inline float unit_dot(const u32 w[16], const u32 x[16], float s0, float s1, float acc) {
-    if constexpr (FMT == FMT_E2M1) {
+    if constexpr (Fmt<FMT>::TWO_SCALES) {
         float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
@@ -207,7 +246,7 @@ __device__ inline float unit_dot(const u32 w[16], const u32 x[16], float s0, flo
 template <int FMT>
 __device__ inline float unit_dot_split(const u32 w[16], const u32 xh[16], const u32 xl[16], float s0, float s1,
                                        float acc) {
-    if constexpr (FMT == FMT_E2M1) {
+    if constexpr (Fmt<FMT>::TWO_SCALES) {
         float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -232,11 +271,17 @@ __device__ inline float unit_dot_split(const u32 w[16], const u32 xh[16], const 
     }
 }
 
+// The unit's block scale(s) as fp32: e4m3 and UE8M0 bytes through the LDS
+// table, fp16 by the exact hardware conversion.
 template <int FMT>
 __device__ inline void unit_scales(const Unit<FMT> &U, const Luts &L, float &s0, float &s1) {
-    if constexpr (FMT == FMT_E2M1) {
+    using F = Fmt<FMT>;
+    if constexpr (F::TWO_SCALES) {
         s0 = L.scale[U.s & 0xFF];
         s1 = L.scale[(U.s >> 8) & 0xFF];
+    } else if constexpr (F::SCALE == SC_FP16) {
+        s0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(U.s & 0xFFFF));
+        s1 = 0.f;
     } else {
         s0 = L.scale[U.s & 0xFF];
         s1 = 0.f;

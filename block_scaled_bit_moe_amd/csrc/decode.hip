@@ -6,18 +6,27 @@
 
 namespace moeq {
 
-hipError_t decode_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decode_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
-hipError_t decode_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decode_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
-hipError_t decode1_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decode1_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
-hipError_t decode1_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decode1_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
-hipError_t decodeT_launch_e2m1_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decodeT_launch_e2m1_hw(const DecodeArgs &a, hipStream_t s);
-hipError_t decodeT_launch_e2m3_lut(const DecodeArgs &a, hipStream_t s);
-hipError_t decodeT_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s);
+template <> DecodeFns decode_fns_for<1, DEC_LUT>();
+template <> DecodeFns decode_fns_for<1, DEC_HW>();
+template <> DecodeFns decode_fns_for<2, DEC_LUT>();
+template <> DecodeFns decode_fns_for<2, DEC_HW>();
+template <> DecodeFns decode_fns_for<3, DEC_LUT>();
+template <> DecodeFns decode_fns_for<3, DEC_HW>();
+template <> DecodeFns decode_fns_for<4, DEC_LUT>();
+template <> DecodeFns decode_fns_for<4, DEC_HW>();
+template <> DecodeFns decode_fns_for<5, DEC_LUT>();
+template <> DecodeFns decode_fns_for<5, DEC_HW>();
+
+static DecodeFns fns_of(int fmt, int dec) {
+    const bool hw = dec == DEC_HW;
+    switch (fmt) {
+        case 1: return hw ? decode_fns_for<1, DEC_HW>() : decode_fns_for<1, DEC_LUT>();
+        case 2: return hw ? decode_fns_for<2, DEC_HW>() : decode_fns_for<2, DEC_LUT>();
+        case 3: return hw ? decode_fns_for<3, DEC_HW>() : decode_fns_for<3, DEC_LUT>();
+        case 4: return hw ? decode_fns_for<4, DEC_HW>() : decode_fns_for<4, DEC_LUT>();
+        default: return hw ? decode_fns_for<5, DEC_HW>() : decode_fns_for<5, DEC_LUT>();
+    }
+}
 
 // MOEQ_DECODE1=0 routes single-token calls, MOEQ_DECODET=0 routed calls of
 // 2..16 tokens, to the general kernel (for A/B measurement; all give
@@ -46,22 +55,18 @@ size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s) {
+    const DecodeFns f = fns_of(a.L.fmt, dec);
     if (a.T == 1 && a.mode == MODE_ROUTE && single_token_kernel_enabled()) {
-        hipError_t e;
-        if (a.L.fmt == 1) e = dec == DEC_HW ? decode1_launch_e2m1_hw(a, s) : decode1_launch_e2m1_lut(a, s);
-        else e = dec == DEC_HW ? decode1_launch_e2m3_hw(a, s) : decode1_launch_e2m3_lut(a, s);
+        const hipError_t e = f.one(a, s);
         if (e != hipErrorNotSupported) return e;
         (void)hipGetLastError();
     }
     if (a.T >= 2 && a.T <= DEC_MAX_T && a.mode == MODE_ROUTE && few_token_kernel_enabled()) {
-        hipError_t e;
-        if (a.L.fmt == 1) e = dec == DEC_HW ? decodeT_launch_e2m1_hw(a, s) : decodeT_launch_e2m1_lut(a, s);
-        else e = dec == DEC_HW ? decodeT_launch_e2m3_hw(a, s) : decodeT_launch_e2m3_lut(a, s);
+        const hipError_t e = f.few(a, s);
         if (e != hipErrorNotSupported) return e;
         (void)hipGetLastError();
     }
-    if (a.L.fmt == 1) return dec == DEC_HW ? decode_launch_e2m1_hw(a, s) : decode_launch_e2m1_lut(a, s);
-    return dec == DEC_HW ? decode_launch_e2m3_hw(a, s) : decode_launch_e2m3_lut(a, s);
+    return f.general(a, s);
 }
 
 }  // namespace moeq

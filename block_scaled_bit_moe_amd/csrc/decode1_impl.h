@@ -138,7 +138,7 @@ __device__ inline int d1_piece_swz(int u) { return (u >> 1) & 7; }
 
 template <int FMT, int DEC, int QG, int QD, int MG, int MD>
 __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Plan plan) {
-    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
+    constexpr int PAIR = (DEC == DEC_LUT) ? (Fmt<FMT>::SIX ? LUT_E2M3_PAIR : LUT_E2M1_PAIR) : 1;
     __shared__ u32 s_pair[PAIR];
     __shared__ float s_scale[LUT_SCALE];
     __shared__ D1Shared S;

@@ -52,9 +52,9 @@ __host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 1 : 2; }
 // gives every workgroup an equal share of this cost rather than of the rows,
 // so that workgroups holding experts with several tokens get fewer rows.  The
 // constants are the ratios measured on a 6144-wide layer with 2048-wide
-// experts (e2m3 rows carry 6.25 instead of 4.5 bits per weight).
-template <int FMT> __host__ __device__ constexpr int dt_cost_gu(int m) { return (FMT == FMT_E2M1 ? 6 : 8) + 2 * m; }
-template <int FMT> __host__ __device__ constexpr int dt_cost_dn(int m) { return (FMT == FMT_E2M1 ? 3 : 4) + 2 * m; }
+// experts (six-bit codes carry 6.25 instead of 4.5 bits per weight).
+template <int FMT> __host__ __device__ constexpr int dt_cost_gu(int m) { return (Fmt<FMT>::SIX ? 8 : 6) + 2 * m; }
+template <int FMT> __host__ __device__ constexpr int dt_cost_dn(int m) { return (Fmt<FMT>::SIX ? 4 : 3) + 2 * m; }
 
 // The first group g with cum[g + 1] > c (cum ascending, cum[0] = 0, c < cum[n]).
 __device__ inline int dt_first_group(const int *cum, int n, int c) {
@@ -157,7 +157,7 @@ __host__ __device__ inline size_t dt_lds_bytes(int units, int W, int slots) {
 // which a shared expert always has at T > 4.
 template <int FMT, int DEC, int QG, int QD, int XT>
 __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPlan plan) {
-    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
+    constexpr int PAIR = (DEC == DEC_LUT) ? (Fmt<FMT>::SIX ? LUT_E2M3_PAIR : LUT_E2M1_PAIR) : 1;
     __shared__ u32 s_pair[PAIR];
     __shared__ float s_scale[LUT_SCALE];
     __shared__ DTShared S;

@@ -1,11 +1,4 @@
-// decode_e2m3_hw.hip -- one (format, decoder) instantiation set of the
-// single-launch MoE decode kernel (decode_impl.h), compiled on its own.
-#include "decode1_impl.h"
-#include "decodeT_impl.h"
-#include "decode_impl.h"
+// decode_e2m3_hw.hip -- the decode kernels for format e2m3, hw decoder.
+#include "decode_inst.h"
 
-namespace moeq {
-hipError_t decode_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s) { return decode_fd<FMT_E2M3, DEC_HW>(a, s); }
-hipError_t decode1_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s) { return decode1_fd<FMT_E2M3, DEC_HW>(a, s); }
-hipError_t decodeT_launch_e2m3_hw(const DecodeArgs &a, hipStream_t s) { return decodeT_fd<FMT_E2M3, DEC_HW>(a, s); }
-}  // namespace moeq
+MOEQ_DECODE_INSTANCE(FMT_E2M3, DEC_HW)

@@ -138,7 +138,7 @@ __device__ inline void route_tokens(const DecodeArgs &a, int T, int E, int k, in
 
 template <int FMT, int DEC, int QG, int QD, int MT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    constexpr int PAIR = (DEC == DEC_LUT) ? (FMT == FMT_E2M1 ? LUT_E2M1_PAIR : LUT_E2M3_PAIR) : 1;
+    constexpr int PAIR = (DEC == DEC_LUT) ? (Fmt<FMT>::SIX ? LUT_E2M3_PAIR : LUT_E2M1_PAIR) : 1;
     __shared__ u32 s_pair[PAIR];
     __shared__ float s_scale[LUT_SCALE];
     __shared__ DecShared<MT> S;

@@ -72,6 +72,22 @@ hipError_t launch_gemv(int fmt, int dec, const uint8_t *codes, const uint8_t *sc
                        const uint16_t *x, int B, void *y, int out_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s);
 
+// The dense GEMV of one (format, decoder) pair (gemv_<format>.hip).
+typedef hipError_t (*GemvFn)(const uint8_t *codes, const uint8_t *scales, int rows, int cols, const uint16_t *x,
+                             int B, void *y, int out_f32, hipStream_t s);
+template <int FMT, int DEC> GemvFn gemv_fn_for();
+
+// The decode launchers of one (format, decoder) pair, each defined in its own
+// translation unit (decode_<format>_<decoder>.hip).  A launcher returns
+// hipErrorNotSupported when the call's shape is outside what its kernel takes.
+typedef hipError_t (*DecodeFn)(const DecodeArgs &, hipStream_t);
+struct DecodeFns {
+    DecodeFn general;   // any T <= 16, fixed-expert calls
+    DecodeFn one;       // T == 1
+    DecodeFn few;       // 2 <= T <= 16
+};
+template <int FMT, int DEC> DecodeFns decode_fns_for();
+
 int decoder_choice();    // DEC_LUT or DEC_HW (MOEQ_DECODER=lut|hw, read once)
 
 // The library-owned workspace of moe_layer_decode_noalloc (noalloc.hip): a

@@ -12,7 +12,7 @@
 //   gate/up  per (block, tile of 64 intermediate rows): g = Wg x, u = Wu x
 //            on MFMA 16x16x32 bf16 with fp32 accumulation, then
 //            h = silu(g) * u, stored as a bf16 hi + lo pair
-//   down     per (block, tile of 512 hidden rows, 256 for e2m3): y = Wd (h_hi + h_lo)
+//   down     per (block, tile of 512 hidden rows, 256 for six-bit codes): y = Wd (h_hi + h_lo)
 //            into fp32 partials, one row per (token, expert) pair
 //   combine  per token: sum of w_r * y_r in rank order, plus the shared
 //            expert, rounded once to bf16
@@ -20,9 +20,10 @@
 // Weights.  Each wave owns 16-row groups of the weight tile for the whole K
 // range, so no other wave needs its decoded weights: a lane loads one unit
 // (32 consecutive weights of one row) per 128-wide K step, decodes it with
-// the hardware conversion and multiplies in the block scale (exact: every
-// product of a code value and a scale has at most 5 significant bits and
-// stays in bf16's range), which gives the B operand of four MFMAs directly.
+// the hardware conversion and multiplies in the block scale (exact for the
+// minifloat formats: a code value times its scale has at most 8 significant
+// bits; int4 times its fp16 scale is carried as two bf16 parts), which gives
+// the B operand of four MFMAs directly (pf_unit_to_b).
 // Lane l covers row l%16 and the K sub-range 32*(l/16) .. +32 of each step;
 // MFMA step s takes weights 8s..8s+7 of that sub-range, so within one
 // instruction the four lane groups contribute K offsets {8s, 32+8s, 64+8s,
@@ -53,8 +54,11 @@ constexpr int PF_ROW = PF_KS * 2 + 16;      // bytes per staged activation row
 constexpr int PF_STAGE = PF_MB * PF_ROW;    // bytes per staged plane
 constexpr int PF_RG_GU = 1;                 // 16-row groups per wave: gate/up (each of gate and up)
 // down: e2m1 takes four (measured: 2 -> 4 took 10 us off the 2,048-token
-// layer); e2m3's larger units would spill registers with four
-template <int FMT> constexpr int pf_rg_dn() { return FMT == FMT_E2M1 ? 4 : 2; }
+// layer); six-bit codes' larger units would spill registers with four
+template <int FMT> constexpr int pf_rg_dn() { return Fmt<FMT>::SIX ? 2 : 4; }
+// int4 weights times their fp16 group scale need up to 14 significant bits, so
+// they enter the matrix cores as two bf16 parts, w = hi + lo exactly
+template <int FMT> constexpr bool pf_split_w() { return Fmt<FMT>::SCALE == SC_FP16; }
 constexpr int PF_PD = 3;                    // weight units in flight per row group (K steps ahead)
 constexpr int PF_MAX_K = 32;                // top-k limit of the layer
 
@@ -225,13 +229,20 @@ __device__ inline Unit<FMT> pf_load_unit(const uint8_t *rc, const uint8_t *rs, i
 
 // Decode one unit, block scale included, into the B operands of the four MFMA
 // steps of a K step (step s takes weights 8s .. 8s+7 of the unit).
-//  e2m1 + e4m3: each byte -> two fp32 values, times the scale (exact: a code
-//    value times an e4m3 scale has at most 5 significant bits), packed to bf16;
-//  e2m3 + UE8M0: the 32-value conversion applies the power-of-two scale
-//    itself (the conversion takes the scale's exponent field, which is all a
-//    UE8M0 scale has).
+//  e2m1 + e4m3 and e2m3 + e4m3: codes -> fp32, times the scale of their block
+//    of 16 (exact: a code value has at most 4 significant bits and an e4m3
+//    scale 4, and the product stays inside bf16's range), packed to bf16;
+//  e2m3 + UE8M0 and e2m1 + UE8M0: the conversion applies the power-of-two
+//    scale itself (it takes the scale's exponent field, which is all a UE8M0
+//    scale has): exact while code value times scale stays inside bf16's range;
+//  int4 + fp16: w = code * scale is exact in fp32 but needs up to 14 bits, so
+//    it is split into bf16 hi = RNE(w) and lo = w - hi (exact, at most 7 bits)
+//    and the matrix cores take both (b and bl).
+__device__ inline u32 pf_pack2(float a, float b) { return __builtin_bit_cast(u32, bf16x2_t{(__bf16)a, (__bf16)b}); }
+
 template <int FMT>
-__device__ inline void pf_unit_to_b(const Unit<FMT> &U, const float *s_scale, bf16x8_t (&b)[4]) {
+__device__ inline void pf_unit_to_b(const Unit<FMT> &U, const float *s_scale, bf16x8_t (&b)[4], bf16x8_t (&bl)[4]) {
+    using F = Fmt<FMT>;
     if constexpr (FMT == FMT_E2M1) {
         const float s0 = s_scale[U.s & 0xFF], s1 = s_scale[(U.s >> 8) & 0xFF];
         const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
@@ -242,18 +253,58 @@ __device__ inline void pf_unit_to_b(const Unit<FMT> &U, const float *s_scale, bf
             const f2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 1);
             const f2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 2);
             const f2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[s], 1.0f, 3);
-            const bf16x2_t p[4] = {bf16x2_t{(__bf16)(f0.x * sc), (__bf16)(f0.y * sc)},
-                                   bf16x2_t{(__bf16)(f1.x * sc), (__bf16)(f1.y * sc)},
-                                   bf16x2_t{(__bf16)(f2.x * sc), (__bf16)(f2.y * sc)},
-                                   bf16x2_t{(__bf16)(f3.x * sc), (__bf16)(f3.y * sc)}};
             u32x4_t v;
-            v[0] = __builtin_bit_cast(u32, p[0]);
-            v[1] = __builtin_bit_cast(u32, p[1]);
-            v[2] = __builtin_bit_cast(u32, p[2]);
-            v[3] = __builtin_bit_cast(u32, p[3]);
+            v[0] = pf_pack2(f0.x * sc, f0.y * sc);
+            v[1] = pf_pack2(f1.x * sc, f1.y * sc);
+            v[2] = pf_pack2(f2.x * sc, f2.y * sc);
+            v[3] = pf_pack2(f3.x * sc, f3.y * sc);
             b[s] = __builtin_bit_cast(bf16x8_t, v);
         }
+    } else if constexpr (FMT == FMT_MXFP4) {
+        const float sc = __builtin_bit_cast(float, (U.s & 0xFFu) << 23);
+        const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4_t v;
+            v[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[s], sc, 0));
+            v[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[s], sc, 1));
+            v[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[s], sc, 2));
+            v[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[s], sc, 3));
+            b[s] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    } else if constexpr (FMT == FMT_INT4) {
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(U.s & 0xFFFF));
+        const u32 d[4] = {U.c.x, U.c.y, U.c.z, U.c.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            u32x4_t vh, vl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float w0 = (float)(((int)(d[s] << (28 - 8 * q))) >> 28) * sc;
+                const float w1 = (float)(((int)(d[s] << (24 - 8 * q))) >> 28) * sc;
+                const u32 h = pf_pack2(w0, w1);
+                vh[q] = h;
+                vl[q] = pf_pack2(w0 - __builtin_bit_cast(float, h << 16), w1 - __builtin_bit_cast(float, h & 0xFFFF0000u));
+            }
+            b[s] = __builtin_bit_cast(bf16x8_t, vh);
+            bl[s] = __builtin_bit_cast(bf16x8_t, vl);
+        }
+    } else if constexpr (FMT == FMT_E2M3S) {
+        u32x6_t v;
+        v[0] = U.c0.x; v[1] = U.c0.y; v[2] = U.c1.x; v[3] = U.c1.y; v[4] = U.c2.x; v[5] = U.c2.y;
+        typedef __attribute__((ext_vector_type(32))) float f32x32_t;
+        const f32x32_t f = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(v, 1.0f);
+        const float s0 = s_scale[U.s & 0xFF], s1 = s_scale[(U.s >> 8) & 0xFF];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float sc = s < 2 ? s0 : s1;
+            u32x4_t q4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) q4[q] = pf_pack2(f[8 * s + 2 * q] * sc, f[8 * s + 2 * q + 1] * sc);
+            b[s] = __builtin_bit_cast(bf16x8_t, q4);
+        }
     } else {
+        static_assert(FMT == FMT_E2M3, "format");
         u32x6_t v;
         v[0] = U.c0.x; v[1] = U.c0.y; v[2] = U.c1.x; v[3] = U.c1.y; v[4] = U.c2.x; v[5] = U.c2.y;
         const float sc = __builtin_bit_cast(float, (U.s & 0xFFu) << 23);
@@ -267,11 +318,12 @@ __device__ inline void pf_unit_to_b(const Unit<FMT> &U, const float *s_scale, bf
             b[s] = __builtin_bit_cast(bf16x8_t, q);
         }
     }
+    (void)F::SIX;
 }
 
 template <int FMT>
 __device__ inline void pf_zero_unit(Unit<FMT> &U) {
-    if constexpr (FMT == FMT_E2M1) {
+    if constexpr (!Fmt<FMT>::SIX) {
         U.c = make_uint4(0u, 0u, 0u, 0u);
     } else {
         U.c0 = make_uint2(0u, 0u);
@@ -298,7 +350,7 @@ __device__ inline void pf_wait_vm() {
 }
 
 // Vector-memory loads of one weight unit.
-template <int FMT> struct PfUnitLoads { static constexpr int n = FMT == FMT_E2M1 ? 2 : 4; };
+template <int FMT> struct PfUnitLoads { static constexpr int n = Fmt<FMT>::SIX ? 4 : 2; };
 
 // Grouped GEMM main loop for a block of NSUB 16-token sub-tiles.
 //
@@ -415,9 +467,10 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
 #pragma unroll
             for (int j = 0; j < NB; ++j) pf_zero_unit<FMT>(wq[d][j]);
         }
-        bf16x8_t bw[NB][4];
+        constexpr bool WLO = pf_split_w<FMT>();
+        bf16x8_t bw[NB][4], bwl[NB][4];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) pf_unit_to_b<FMT>(wq[d][j], s_scale, bw[j]);
+        for (int j = 0; j < NB; ++j) pf_unit_to_b<FMT>(wq[d][j], s_scale, bw[j], bwl[j]);
         issue_stage(std::integral_constant<int, dn>{}, it + PF_PD);
         load_w(wq[dn], it + PF_PD);
         const uint8_t *st = stage(dc);
@@ -438,6 +491,11 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
                     acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bw[j][s], acc[j][m], 0, 0, 0);
                     if (DOWN)
                         acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bw[j][s], acc[j][m], 0, 0, 0);
+                    if (WLO) {
+                        acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bwl[j][s], acc[j][m], 0, 0, 0);
+                        if (DOWN)
+                            acc[j][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bwl[j][s], acc[j][m], 0, 0, 0);
+                    }
                 }
         }
     };
@@ -482,7 +540,7 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
 
 // Grouped GEMM over the block list.  gate/up (DOWN = false): 4 waves, each
 // with 16 rows of gate and the same 16 rows of up; down: 8 waves of 64 rows
-// (e2m1) or 32 rows (e2m3).
+// (four-bit codes) or 32 rows (six-bit codes).
 template <int FMT, bool DOWN>
 __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel(PfArgs a, int NT) {
     constexpr int NWAVES = DOWN ? 8 : 4;
@@ -518,7 +576,7 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int lr = lane & 15;
 
-    if (FMT == FMT_E2M1) {
+    if (Fmt<FMT>::SCALE == SC_E4M3) {   // the other scales are converted arithmetically
         Luts Lt;
         Lt.pair = nullptr;
         Lt.scale = s_scale;

@@ -100,7 +100,14 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
             hipError_t e = launch_route(a.logits + (size_t)c0 * L.E, Tc, L.E, L.k, idx, w, s);
             if (e != hipSuccess) return e;
         }
-        hipError_t e = L.fmt == 1 ? pf_chunk<FMT_E2M1>(p, l, s) : pf_chunk<FMT_E2M3>(p, l, s);
+        hipError_t e;
+        switch (L.fmt) {
+            case FMT_E2M1: e = pf_chunk<FMT_E2M1>(p, l, s); break;
+            case FMT_E2M3: e = pf_chunk<FMT_E2M3>(p, l, s); break;
+            case FMT_MXFP4: e = pf_chunk<FMT_MXFP4>(p, l, s); break;
+            case FMT_INT4: e = pf_chunk<FMT_INT4>(p, l, s); break;
+            default: e = pf_chunk<FMT_E2M3S>(p, l, s); break;
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

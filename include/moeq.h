@@ -33,6 +33,14 @@
  *                                                    [6j, 6j+6) of the row read
  *                                                    as a little-endian bit string
  *                           scales [rows][cols/128] UE8M0: value 2^(b-127)
+ *   MOE_FMT_E2M1_UE8M0_B32  codes  as format 1
+ *                           scales [rows][cols/32]  UE8M0
+ *   MOE_FMT_INT4_F16_B64    codes  as format 1, each nibble a two's-complement
+ *                                                    integer -8..7
+ *                           scales [rows][cols/64]  IEEE binary16, two bytes
+ *                                                    each, low byte first
+ *   MOE_FMT_E2M3_E4M3_B16   codes  as format 2
+ *                           scales [rows][cols/16]  fp8 e4m3 as format 1
  *   Weight W[r][j] = value(code) * value(scale[r][j / block]); e2m1 and e2m3
  *   have one sign bit, two exponent bits of bias 1 and 1 or 3 mantissa bits,
  *   with subnormals at exponent field 0 and no Inf/NaN codes.
@@ -88,10 +96,16 @@ enum {
     MOE_EKERNEL = -5        /* a kernel's bounded wait expired (moe_workspace_status) */
 };
 
-/* Weight formats. */
+/* Weight formats.  1 and 2 are the formats of knivesysl README, "formats";
+ * 3 and 4 the expert containers of colibri README's model notes (MXFP4
+ * experts; the group-scaled "gs64" int4 container of "Get the model"); 5 pairs
+ * the six-bit elements with the e4m3 scale per 16. */
 enum {
     MOE_FMT_E2M1_E4M3_B16 = 1,    /* 4-bit e2m1, one fp8-e4m3 scale per 16 weights */
-    MOE_FMT_E2M3_UE8M0_B128 = 2   /* 6-bit e2m3, one UE8M0 (power-of-two) scale per 128 */
+    MOE_FMT_E2M3_UE8M0_B128 = 2,  /* 6-bit e2m3, one UE8M0 (power-of-two) scale per 128 */
+    MOE_FMT_E2M1_UE8M0_B32 = 3,   /* MXFP4: 4-bit e2m1, one UE8M0 scale per 32 */
+    MOE_FMT_INT4_F16_B64 = 4,     /* 4-bit two's-complement integers, one fp16 scale per 64 */
+    MOE_FMT_E2M3_E4M3_B16 = 5     /* 6-bit e2m3, one fp8-e4m3 scale per 16 */
 };
 
 /* Flags. */
@@ -114,7 +128,7 @@ enum {
 #define MOE_MAX_DIM 32768        /* hidden, inter, rows and cols */
 
 /* A block-scaled matrix [rows][cols]; y = W x reduces over cols.
- * cols must be a multiple of 32 (e2m1) or 128 (e2m3). */
+ * cols must be a multiple of 32 (formats 1 and 3), 64 (4 and 5) or 128 (2). */
 typedef struct moe_qmat {
     int32_t fmt;
     int32_t rows;
@@ -125,7 +139,7 @@ typedef struct moe_qmat {
 } moe_qmat;
 
 /* One MoE layer.  hidden and inter (and shared_inter when nonzero) must be
- * multiples of 32 (e2m1) or 128 (e2m3). */
+ * multiples of 32 (formats 1 and 3), 64 (4 and 5) or 128 (2). */
 typedef struct moe_layer {
     int32_t fmt;
     int32_t hidden;          /* H */

@@ -67,7 +67,7 @@ def test_route_validation(lib):
 
 
 @pytest.mark.parametrize("field,value,needle", [
-    ("fmt", 3, "fmt"), ("hidden", 48, "hidden"), ("inter", 0, "inter"), ("n_experts", 0, "n_experts"),
+    ("fmt", 6, "fmt"), ("fmt", 0, "fmt"), ("hidden", 48, "hidden"), ("inter", 0, "inter"), ("n_experts", 0, "n_experts"),
     ("top_k", 9, "top_k"), ("top_k", 0, "top_k"), ("shared_inter", -32, "shared_inter"),
     ("w13_codes", 0, "w13_codes"), ("w2_scales", FAKE + 8, "w2_scales"), ("shared_inter", 48, "shared_inter"),
 ])
