@@ -54,6 +54,9 @@ def _load():
     lib.oracle_code_row_bytes.restype = i64
     lib.oracle_scale_row_bytes.argtypes = [i32, i64]
     lib.oracle_scale_row_bytes.restype = i64
+    lib.oracle_rmsnorm.argtypes = [i64, i64, vp, vp, ctypes.c_double, vp]
+    lib.oracle_router_logits.argtypes = [i64, i64, i64, vp, vp, vp]
+    lib.oracle_residual_add.argtypes = [i64, vp, vp, vp]
     lib.oracle_threads.argtypes = [i32]
     lib.oracle_threads.restype = i32
     lib.oracle_init()
@@ -208,6 +211,54 @@ def layer(fmt, H, I, E, k, experts, x_bf16, logits, shared=None, shared_inter=0,
     if rc:
         raise ValueError("oracle.layer failed: %d" % rc)
     return idx, w, out
+
+
+def rmsnorm(x_bf16, gamma_bf16, eps):
+    """y = x * g / sqrt(mean(x^2) + eps) per token, in double (x [T][H], g [H] bf16 bits)."""
+    x, px = _c(np.atleast_2d(x_bf16), np.uint16)
+    g, pg = _c(gamma_bf16, np.uint16)
+    T, H = x.shape
+    assert g.size == H
+    y = np.empty((T, H), np.float64)
+    _load().oracle_rmsnorm(T, H, px, pg, float(eps), y.ctypes.data)
+    return y
+
+
+def router_logits(x_bf16, wr_bf16):
+    """Router scores in double: logits[t][e] = Wr[e] . x[t] (Wr [E][H], x [T][H] bf16 bits)."""
+    x, px = _c(np.atleast_2d(x_bf16), np.uint16)
+    wr, pw = _c(np.atleast_2d(wr_bf16), np.uint16)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == H
+    out = np.empty((T, E), np.float64)
+    _load().oracle_router_logits(T, H, E, px, pw, out.ctypes.data)
+    return out
+
+
+def residual_add(r_bf16, y):
+    r, pr = _c(r_bf16, np.uint16)
+    y, py = _c(y, np.float64)
+    assert r.shape == y.shape
+    out = np.empty(y.shape, np.float64)
+    _load().oracle_residual_add(y.size, pr, py, out.ctypes.data)
+    return out
+
+
+def block(fmt, H, I, E, k, experts, x_bf16, gamma_bf16, wr_bf16, eps, shared=None, shared_inter=0,
+          out_rows=None):
+    """The whole MoE block for T tokens of the residual stream x:
+        xn = bf16(RMSNorm(x))              the activation the experts take
+        logits = Wr xn, rounded to fp32    the scores routing ranks
+        out = x + MoE(xn, logits)          the residual add
+    Returns (idx, w, out double, xn bf16 bits, logits double)."""
+    x = np.atleast_2d(np.asarray(x_bf16, np.uint16))
+    xn = bf16_round(rmsnorm(x, gamma_bf16, eps))
+    lg = router_logits(xn, wr_bf16)
+    idx, w, y = layer(fmt, H, I, E, k, experts, xn, lg.astype(np.float32), shared=shared,
+                      shared_inter=shared_inter, out_rows=out_rows)
+    r = x if out_rows is None else x[:, np.asarray(out_rows)]
+    return idx, w, residual_add(np.ascontiguousarray(r), y), xn, lg
 
 
 def use_library(path=None):

@@ -322,6 +322,41 @@ int oracle_layer(int fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
     return 0;
 }
 
+/* The steps either side of the MoE layer (the whole MoE block):
+ *   RMSNorm in front of it (nextsycl README, dense 27B engine: the norm that
+ *   emits the next kernel's input; knivesysl README, "how it works": RMS fused
+ *   into the activation quantisation);
+ *   the router scores that routing ranks (Strata docs/INTEL.md, "Decode
+ *   round 2": scores followed by top-k);
+ *   the residual add after it.  */
+
+/* y[t][i] = x[t][i] * g[i] / sqrt(eps + (1/H) * sum_j x[t][j]^2), x and g bf16. */
+void oracle_rmsnorm(int64_t T, int64_t H, const uint16_t *x, const uint16_t *g, double eps, double *y) {
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *xt = x + t * H;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) ss += bf16_value(xt[j]) * bf16_value(xt[j]);
+        const double r = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t i = 0; i < H; ++i) y[t * H + i] = bf16_value(xt[i]) * bf16_value(g[i]) * r;
+    }
+}
+
+/* logits[t][e] = sum_j Wr[e][j] * x[t][j]: router weights bf16 [E][H], x bf16 [T][H]. */
+void oracle_router_logits(int64_t T, int64_t H, int64_t E, const uint16_t *x, const uint16_t *wr, double *logits) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < H; ++j) acc += bf16_value(wr[e * H + j]) * bf16_value(x[t * H + j]);
+            logits[t * E + e] = acc;
+        }
+}
+
+/* out[t][i] = r[t][i] + y[t][i]: the residual stream r (bf16) plus the block's output. */
+void oracle_residual_add(int64_t n, const uint16_t *r, const double *y, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_value(r[i]) + y[i];
+}
+
 /* Round a double to bfloat16, once, to nearest with ties to even.  Rounding
  * works on the significand scaled to eight bits (normal range) or on the
  * fixed unit 2^-133 (subnormal range). */

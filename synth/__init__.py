@@ -31,6 +31,7 @@ _lib = None
 K_W13_CODES, K_W13_SCALES, K_W2_CODES, K_W2_SCALES = 1, 2, 3, 4
 K_X, K_LOGITS = 5, 6
 K_W_CODES, K_W_SCALES = 7, 8
+K_GAMMA, K_ROUTER = 9, 10
 
 
 def stream_id(kind: int, sub: int) -> int:
@@ -53,6 +54,7 @@ def _load():
     lib.synth_ue8m0_uniform.argtypes = [u64, u64, u64, u64, ctypes.c_int, ctypes.c_int, vp]
     lib.synth_normal_bf16.argtypes = [u64, u64, u64, u64, d, vp]
     lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, d, vp]
+    lib.synth_normal_bf16_mean.argtypes = [u64, u64, u64, u64, d, d, vp]
     lib.synth_bf16_from_double.argtypes = [d]
     lib.synth_bf16_from_double.restype = ctypes.c_uint16
     lib.synth_fp16_loguniform.argtypes = [u64, u64, u64, u64, d, d, vp]
@@ -200,6 +202,19 @@ def hidden_states(cfg, tokens=None, sub=0) -> np.ndarray:
 def router_logits(cfg, tokens=None, sub=0) -> np.ndarray:
     T = cfg.tokens if tokens is None else tokens
     return normal_f32(cfg.seed, stream_id(K_LOGITS, sub), T * cfg.experts, cfg.logit_sigma).reshape(T, cfg.experts)
+
+
+def norm_gamma(cfg) -> np.ndarray:
+    """RMSNorm gains, bf16 bits [H]: 1 + N(0, gamma_sigma)."""
+    out = np.empty(cfg.hidden, np.uint16)
+    _load().synth_normal_bf16_mean(cfg.seed, stream_id(K_GAMMA, 0), 0, cfg.hidden, 1.0, cfg.gamma_sigma, _ptr(out))
+    return out
+
+
+def router_weights(cfg) -> np.ndarray:
+    """Router weights, bf16 bits [E][H]: N(0, logit_sigma / sqrt(H))."""
+    sigma = cfg.logit_sigma / float(np.sqrt(cfg.hidden))
+    return normal_bf16(cfg.seed, stream_id(K_ROUTER, 0), cfg.experts * cfg.hidden, sigma).reshape(cfg.experts, cfg.hidden)
 
 
 # ---------------------------------------------------------------- dense GEMV

@@ -32,6 +32,11 @@ class MoEConfig:
     scale_log2: Tuple[float, float] = (-6.0, -2.0)   # e4m3 scales: 2^U[lo, hi)
     ue8m0_exp: Tuple[int, int] = (-8, -3)           # UE8M0 scales: 2^e, e uniform integer
     fp16_log2: Tuple[float, float] = (-8.0, -4.0)   # fp16 scales (int4): 2^U[lo, hi)
+    # the steps either side (the whole block): RMSNorm gains ~ 1 + N(0, gamma_sigma)
+    # in bf16, its epsilon, and router weights ~ N(0, logit_sigma / sqrt(hidden))
+    # in bf16, so that the scores of a unit-RMS activation have spread logit_sigma
+    norm_eps: float = 1e-6
+    gamma_sigma: float = 0.1
     seed: int = 0
     description: str = ""
 
@@ -63,4 +68,12 @@ BATCHED = MoEConfig("batched_decode", tokens=16, hidden=6144, experts=288, top_k
 PREFILL = MoEConfig("prefill", tokens=2048, hidden=2048, experts=512, top_k=10, inter=512,
                     description="prefill MoE layer: 2048 tokens, H=2048, 512 experts, top-10, I=512")
 
-ALL = {c.name: c for c in (TOY, GEMV, WIDE, BATCHED, PREFILL)}
+# The wide decode layer with the steps either side: RMSNorm, router scores and
+# top-k, the MoE layer, the residual add.
+WIDE_BLOCK = MoEConfig("wide_block", tokens=1, hidden=2048, experts=512, top_k=10, inter=512, shared_inter=512,
+                       logit_sigma=1.5,
+                       description="wide MoE block: RMSNorm, router GEMV + top-10 of 512, the layer, residual add")
+BATCHED_BLOCK = MoEConfig("batched_block", tokens=16, hidden=6144, experts=288, top_k=8, inter=2048,
+                          description="batched MoE block: RMSNorm, router GEMV + top-8 of 288, the layer, residual add")
+
+ALL = {c.name: c for c in (TOY, GEMV, WIDE, BATCHED, PREFILL, WIDE_BLOCK, BATCHED_BLOCK)}

@@ -152,6 +152,14 @@ void synth_normal_bf16(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t
         out[i] = bf16_from_double(sigma * normal_at(key, offset + (uint64_t)i));
 }
 
+/* bf16 of mean + sigma * N(0,1), rounded once (gains around a mean). */
+void synth_normal_bf16_mean(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t n, double mean,
+                            double sigma, uint16_t *out) {
+    const uint64_t key = stream_key(seed, stream);
+    #pragma omp parallel for schedule(static) if (n > (1u << 18))
+    for (int64_t i = 0; i < (int64_t)n; ++i) out[i] = bf16_from_double(mean + sigma * normal_at(key, offset + (uint64_t)i));
+}
+
 void synth_normal_f32(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t n,
                       double sigma, float *out) {
     const uint64_t key = stream_key(seed, stream);

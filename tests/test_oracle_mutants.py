@@ -39,6 +39,11 @@ MUTANTS = {
     "fp16_byte_order": ("(unsigned)g[0] | ((unsigned)g[1] << 8)", "(unsigned)g[1] | ((unsigned)g[0] << 8)"),
     "fp16_bias": ("ldexp(1.0 + (double)m / 1024.0, (int)e - 15)", "ldexp(1.0 + (double)m / 1024.0, (int)e - 16)"),
     "fp16_subnormal": ("ldexp((double)m / 1024.0, -14)", "ldexp((double)m / 1024.0, -15)"),
+    "rmsnorm_no_eps": ("sqrt(ss / (double)H + eps)", "sqrt(ss / (double)H)"),
+    "rmsnorm_sum_not_mean": ("sqrt(ss / (double)H + eps)", "sqrt(ss + eps)"),
+    "rmsnorm_no_gain": ("y[t * H + i] = bf16_value(xt[i]) * bf16_value(g[i]) * r;", "y[t * H + i] = bf16_value(xt[i]) * r;"),
+    "router_transposed": ("bf16_value(wr[e * H + j])", "bf16_value(wr[j * E + e])"),
+    "residual_dropped": ("out[i] = bf16_value(r[i]) + y[i];", "out[i] = y[i];"),
     "e2m3_e4m3_block": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_E4M3[srow[j / 128]]"),
     "e2m3_e4m3_scale_kind": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_UE8M0[srow[j / 16]]"),
     "ue8m0_bias": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
@@ -193,8 +198,29 @@ def _pin_formats():
         assert np.array_equal(W, expect)
 
 
+def _pin_block():
+    """RMSNorm one-hot and constant rows, router scores against a numpy matmul
+    (E != H), residual add of known values."""
+    H = 256
+    g = np.full(H, 0x3F80, np.uint16)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 3] = 0x4080                                         # 4.0
+    y = oracle.rmsnorm(x, g, 0.0)[0]
+    assert y[3] == 16.0 and not np.delete(y, 3).any()
+    xc = np.full((1, H), 0x4040, np.uint16)                   # 3.0
+    assert np.allclose(oracle.rmsnorm(xc, g, 0.5)[0], 3.0 / np.sqrt(9.5), rtol=1e-15, atol=0)
+    g2 = np.full(H, 0x4000, np.uint16)                        # gain 2
+    assert oracle.rmsnorm(x, g2, 0.0)[0][3] == 32.0
+    cfg = MoEConfig("r", tokens=2, hidden=96, experts=40, top_k=3, inter=32)
+    xr, wr = synth.hidden_states(cfg), synth.router_weights(cfg)
+    f = lambda a: np.array([[oracle.bf16_value(int(b)) for b in r] for r in a])
+    ref = f(xr) @ f(wr).T
+    assert np.allclose(oracle.router_logits(xr, wr), ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    assert list(oracle.residual_add(np.array([0x3FC0, 0xC000], np.uint16), np.array([0.25, 0.5]))) == [1.75, -1.5]
+
+
 PINS = [_pin_tables, _pin_packing, _pin_scale_blocks, _pin_gemv, _pin_route, _pin_silu, _pin_ffn_and_layer,
-        _pin_formats]
+        _pin_formats, _pin_block]
 
 
 def _failures():
