@@ -54,7 +54,11 @@ def kernel_of(workload, batch=1):
     if workload == "dense_gemv_e2m3":
         return "gemv_reg_kernel" if batch == 1 else "gemv_lds_kernel"
     return {"wide_decode": "decode1_kernel", "toy_decode": "decode1_kernel",
-            "batched_decode": "decodeT_kernel", "prefill": "layer_step"}.get(workload, "kernel")
+            "batched_decode": "decodeT_kernel", "prefill": "layer_step",
+            "wide_block": "block_step", "batched_block": "block_step"}.get(workload, "kernel")
+
+
+FMT_NAMES = {1: "e2m1+e4m3/16", 2: "e2m3+ue8m0/128", 3: "e2m1+ue8m0/32", 4: "int4+fp16/64", 5: "e2m3+e4m3/16"}
 
 
 def parse():
@@ -64,6 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default=DEFAULT_CONFIG)
     p.add_argument("--batch", type=int, default=1, help="GEMV tokens (dense_gemv_e2m3 only)")
+    p.add_argument("--fmt", type=int, default=0,
+                   help="weight format of the workload (1..5; 0: the workload's own): measures the format variants")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0: enough for >= 4x the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -313,6 +319,18 @@ def cpu_baseline_moe(cfg, seconds, logits_list, x, slice_tokens=None):
     return tokens, spent
 
 
+def oracle_bf16_rmsnorm(x, gamma, eps):
+    """The block's normalised activation as the oracle computes it (bookkeeping
+    of which experts a block call selects)."""
+    import oracle
+    return oracle.bf16_round(oracle.rmsnorm(x, gamma, eps))
+
+
+def router_scores(xn, wr):
+    import oracle
+    return oracle.router_logits(xn, wr).astype(np.float32)
+
+
 def cpu_figures(run_sample, seconds, cores):
     """The oracle timed on all `cores` threads (~`seconds`) and on one thread
     (~seconds / 2).  run_sample(budget) returns (work units done, seconds,
@@ -324,6 +342,34 @@ def cpu_figures(run_sample, seconds, cores):
     n_one, el_one, what_one = run_sample(seconds / 2)
     oracle.set_threads(cores)
     return (n_all / el_all, what_all), (n_one / el_one, what_one)
+
+
+def cpu_baseline_block(cfg, seconds, xs_host):
+    """The oracle's whole block (norm, scores, routing, layer, residual) call
+    after call on the host cores until ~`seconds` of oracle time.  Returns
+    (tokens, seconds, sample text)."""
+    import oracle
+    import synth
+    g, wr = synth.norm_gamma(cfg), synth.router_weights(cfg)
+    sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
+    cache, spent, done, tokens = {}, 0.0, 0, 0
+    while spent < seconds:
+        x = xs_host[done % len(xs_host)]
+        lg = router_scores(oracle_bf16_rmsnorm(x, g, cfg.norm_eps), wr)
+        ex = {}
+        for e in np.unique(oracle.route(lg, cfg.top_k)[0]):
+            e = int(e)
+            if e not in cache:
+                cache[e] = synth.expert_weights(cfg, e)
+            ex[e] = cache[e]
+        t1 = time.perf_counter()
+        oracle.block(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, x, g, wr, cfg.norm_eps, shared=sh,
+                     shared_inter=cfg.shared_inter)
+        spent += time.perf_counter() - t1
+        done += 1
+        tokens += x.shape[0]
+    return tokens, spent, "%d token(s) of the workload (whole blocks, fresh inputs); %.1f s of oracle time" % (
+        tokens, spent)
 
 
 def main():
@@ -346,6 +392,9 @@ def main():
         sys.exit(1)
     moeq.load_library()
     cfg = configs.ALL[a.config]
+    if a.fmt:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, fmt=a.fmt)
     cores = len(os.sched_getaffinity(0))
     omp = int(os.environ.get("OMP_NUM_THREADS", cores))
     errs = None
@@ -375,7 +424,7 @@ def main():
         tokens_per_s = B / per
         achieved = wbytes / per / 1e9
         metric_value = tokens_per_s
-        workload = {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols, "batch": B, "fmt": "e2m3+ue8m0/128",
+        workload = {"workload": cfg.name, "rows": cfg.rows, "cols": cfg.cols, "batch": B, "fmt": FMT_NAMES[cfg.fmt],
                     "replicas": R}
         kernel = kernel_of(cfg.name, B)
         import oracle
@@ -416,14 +465,29 @@ def main():
         layers = [moeq.Layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, *routed[i % R],
                              shared_inter=cfg.shared_inter, shared=shared_copies[i % n_sh] if n_sh else None)
                   for i in range(n)]
-        logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
-        logits = [torch.from_numpy(l).cuda() for l in logits_host]
+        is_block = cfg.name.endswith("_block")
         xh = synth.hidden_states(cfg)
         x = dev_bf16(xh)
-        ws = moeq.workspace(layers[0], T)
         out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-        calls = [(lambda i=i: moeq.moe_layer_decode(layers[i], x, logits[i % NL], out=out, ws=ws))
-                 for i in range(n)]
+        if is_block:
+            # the whole block: every call gets another residual-stream input (so
+            # other experts) and the router weights are read each call
+            gamma, wr = dev_bf16(synth.norm_gamma(cfg)), dev_bf16(synth.router_weights(cfg))
+            blocks = [moeq.Block(Lr, gamma, wr, cfg.norm_eps) for Lr in layers]
+            xs_host = [synth.hidden_states(cfg, sub=i) for i in range(NL)]
+            xs = [dev_bf16(v) for v in xs_host]
+            ws = moeq.block_workspace(blocks[0], T)
+            calls = [(lambda i=i: moeq.moe_block_decode(blocks[i], xs[i % NL], out=out, ws=ws)) for i in range(n)]
+            logits_host = []
+            for v in xs_host:
+                xn = oracle_bf16_rmsnorm(v, synth.norm_gamma(cfg), cfg.norm_eps)
+                logits_host.append(router_scores(xn, synth.router_weights(cfg)))
+        else:
+            logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
+            logits = [torch.from_numpy(l).cuda() for l in logits_host]
+            ws = moeq.workspace(layers[0], T)
+            calls = [(lambda i=i: moeq.moe_layer_decode(layers[i], x, logits[i % NL], out=out, ws=ws))
+                     for i in range(n)]
         if a.profile_steps:
             for i in range(a.warmup + a.profile_steps):
                 calls[i % len(calls)]()
@@ -439,12 +503,14 @@ def main():
                 for i in range(a.steps)]
         wbytes = float(np.mean(used)) * per_expert if not cfg.shared_inter else \
             float(np.mean([u - 1 for u in used])) * per_expert + bytes_per_expert(cfg, cfg.shared_inter)
+        if is_block:
+            wbytes += cfg.experts * cfg.hidden * 2 + cfg.hidden * 2     # router weights and norm gains
         tokens_per_s = T / per
         achieved = wbytes / per / 1e9
         metric_value = tokens_per_s
         workload = {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "experts": cfg.experts,
                     "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
-                    "fmt": "e2m1+e4m3/16", "replicas": R, "logit_sets": NL, "shared_copies": n_sh,
+                    "fmt": FMT_NAMES[cfg.fmt], "replicas": R, "logit_sets": NL, "shared_copies": n_sh,
                     "experts_read_per_call": float(np.mean(used)), "weight_bytes_per_call": wbytes}
         kernel = kernel_of(cfg.name)
         if many:
@@ -466,13 +532,20 @@ def main():
         idx, _ = oracle.route(lg, cfg.top_k)
         ex = {int(e): synth.expert_weights(cfg, int(e)) for e in np.unique(idx)}
         sh = synth.expert_weights(cfg, cfg.experts) if cfg.shared_inter else None
-        _, _, ref = oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xh[:nt], lg,
-                                 shared=sh, shared_inter=cfg.shared_inter)
+        if is_block:
+            _, _, ref, _, _ = oracle.block(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex,
+                                           xs_host[last % NL][:nt], synth.norm_gamma(cfg), synth.router_weights(cfg),
+                                           cfg.norm_eps, shared=sh, shared_inter=cfg.shared_inter)
+        else:
+            _, _, ref = oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xh[:nt], lg,
+                                     shared=sh, shared_inter=cfg.shared_inter)
         errs = err_figures(outb[:nt], ref)
         errs["sample"] = "%d token(s) of the last timed call" % nt
         cpu = None
         if not a.no_cpu_baseline:
             def sample(budget):
+                if is_block:
+                    return cpu_baseline_block(cfg, budget, xs_host)
                 tok, el = cpu_baseline_moe(cfg, budget, logits_host, xh, slice_tokens=16 if many else None)
                 return tok, el, "%d token(s) of the workload (%s, fresh logits); %.1f s of oracle time" % (
                     tok, "slices of 16 tokens of the chunk" if many else "whole calls", el)

@@ -7,6 +7,7 @@ not on the GPU, the call raises.
 
 Functions carry the C names: moe_route_topk, moe_layer_workspace_bytes,
 moe_expert_ffn_q, moe_layer_decode, moe_layer_decode_noalloc, dense_gemv_q,
+moe_rmsnorm, moe_router_topk_scores, moe_block_workspace_bytes, moe_block_decode,
 moe_workspace_status, moe_last_error, moe_version.
 """
 import ctypes
@@ -50,6 +51,11 @@ class moe_layer(ctypes.Structure):
                 ("sh2_codes", ctypes.c_void_p), ("sh2_scales", ctypes.c_void_p)]
 
 
+class moe_block(ctypes.Structure):
+    _fields_ = [("layer", moe_layer), ("norm_gamma", ctypes.c_void_p), ("router_w", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
 def load_library(path=None):
     """Load libmoeq.so (built in-tree by build.py).  Raises if it is missing."""
     global _lib
@@ -67,12 +73,17 @@ def load_library(path=None):
     lib.moe_layer_decode.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_layer_decode_noalloc.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp]
     lib.dense_gemv_q.argtypes = [ctypes.POINTER(moe_qmat), vp, i32, vp, i32, vp]
+    lib.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]
+    lib.moe_router_topk_scores.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_block_workspace_bytes.argtypes = [ctypes.POINTER(moe_block), i32]
+    lib.moe_block_workspace_bytes.restype = sz
+    lib.moe_block_decode.argtypes = [ctypes.POINTER(moe_block), vp, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.moe_workspace_status.argtypes = [vp, sz, vp]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_version.restype = i32
     for f in ("moe_route_topk", "moe_expert_ffn_q", "moe_layer_decode", "moe_layer_decode_noalloc", "dense_gemv_q",
-              "moe_workspace_status"):
+              "moe_workspace_status", "moe_rmsnorm", "moe_router_topk_scores", "moe_block_decode"):
         getattr(lib, f).restype = i32
     if path is None:
         _lib = lib
@@ -284,6 +295,80 @@ def dense_gemv_q(W, x, y=None, flags=0):
     _check(load_library().dense_gemv_q(ctypes.byref(W.c), _dev(x, "x", _BF16), B,
                                        _dev(y, "y", (torch.bfloat16, torch.float32)), flags, _stream()))
     return y
+
+
+def moe_rmsnorm(x, gamma, eps, y=None, flags=0):
+    """RMSNorm of the T rows of x (bf16 [T][H]) with gains gamma (bf16 [H])."""
+    T, H = x.shape
+    _shape(gamma, "gamma", (H,))
+    y = _out(x, T, H, flags, y)
+    _shape(y, "y", (T, H))
+    _check(load_library().moe_rmsnorm(_dev(x, "x", _BF16), _dev(gamma, "gamma", _BF16), T, H, float(eps),
+                                      _dev(y, "y", (torch.bfloat16, torch.float32)), flags, _stream()))
+    return y
+
+
+def moe_router_topk_scores(x, router_w, k, logits=None, idx=None, w=None, ws=None):
+    """Router scores (fp32 [T][E]) of x (bf16 [T][H]) with router_w (bf16 [E][H]) and their top-k."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    _shape(router_w, "router_w", (E, H))
+    dev = x.device
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if logits is None else logits
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev) if ws is None else ws
+    _shape(logits, "logits", (T, E))
+    _shape(idx, "idx", (T, k))
+    _shape(w, "w", (T, k))
+    _check(load_library().moe_router_topk_scores(_dev(x, "x", _BF16), _dev(router_w, "router_w", _BF16), T, H, E, k,
+                                                 _dev(logits, "logits", (torch.float32,)),
+                                                 _dev(idx, "idx", (torch.int32,)), _dev(w, "w", (torch.float32,)),
+                                                 _dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return logits, idx, w
+
+
+class Block:
+    """A MoE block on the GPU: a Layer plus RMSNorm gains (bf16 [H]) and router
+    weights (bf16 [E][H])."""
+
+    def __init__(self, layer, norm_gamma, router_w, norm_eps=1e-6):
+        _shape(norm_gamma, "norm_gamma", (layer.hidden,))
+        _shape(router_w, "router_w", (layer.n_experts, layer.hidden))
+        self.layer, self.norm_gamma, self.router_w, self.norm_eps = layer, norm_gamma, router_w, norm_eps
+        self.hidden, self.n_experts, self.top_k = layer.hidden, layer.n_experts, layer.top_k
+        self.c = moe_block(layer.c, _dev(norm_gamma, "norm_gamma", _BF16).value,
+                           _dev(router_w, "router_w", _BF16).value, float(norm_eps), 0)
+
+
+def moe_block_workspace_bytes(block, T):
+    n = load_library().moe_block_workspace_bytes(ctypes.byref(block.c), T)
+    if not n:
+        raise MoeError(MOE_EINVAL, moe_last_error())
+    return n
+
+
+def block_workspace(block, T, device=None):
+    return torch.zeros(moe_block_workspace_bytes(block, T), dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_block_decode(block, x, out=None, idx_out=None, w_out=None, flags=0, ws=None):
+    """The MoE block on the residual stream x (bf16 [T][H]): x + layer(RMSNorm(x))."""
+    T = x.shape[0]
+    _shape(x, "x", (T, block.hidden))
+    out = _out(x, T, block.hidden, flags, out)
+    _shape(out, "out", (T, block.hidden))
+    if idx_out is not None:
+        _shape(idx_out, "idx_out", (T, block.top_k))
+    if w_out is not None:
+        _shape(w_out, "w_out", (T, block.top_k))
+    ws = block_workspace(block, T, x.device) if ws is None else ws
+    pi = _dev(idx_out, "idx_out", (torch.int32,)) if idx_out is not None else None
+    pw = _dev(w_out, "w_out", (torch.float32,)) if w_out is not None else None
+    _check(load_library().moe_block_decode(ctypes.byref(block.c), _dev(x, "x", _BF16), T,
+                                           _dev(out, "out", (torch.bfloat16, torch.float32)), pi, pw, flags,
+                                           _dev(ws, "ws", _U8), ws.numel(), _stream()))
+    return out
 
 
 def moe_workspace_status(ws):

@@ -284,6 +284,118 @@ int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *log
     return ok();
 }
 
+static int check_rows(const char *name, int T, int H) {
+    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "%s: T=%d must be in [1, %d]", name, T, MOE_MAX_TOKENS);
+    if (H < 32 || H > MOE_MAX_DIM || H % 32)
+        return fail(MOE_EINVAL, "%s: H=%d must be a multiple of 32 in [32, %d]", name, H, MOE_MAX_DIM);
+    return MOE_OK;
+}
+
+int moe_rmsnorm(const void *x, const void *gamma, int T, int H, float eps, void *y, int flags, void *stream) {
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("gamma", gamma));
+    CHECK(check_ptr("y", y));
+    CHECK(check_rows("moe_rmsnorm", T, H));
+    if (!(eps >= 0.f)) return fail(MOE_EINVAL, "eps=%g must be >= 0", (double)eps);
+    hipError_t e = launch_rmsnorm((const uint16_t *)x, (const uint16_t *)gamma, T, H, eps, y,
+                                  (flags & MOE_OUT_F32) ? 1 : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_rmsnorm launch", e);
+    return ok();
+}
+
+int moe_router_topk_scores(const void *x, const void *router_w, int T, int H, int E, int k, float *logits,
+                           int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("router_w", router_w));
+    CHECK(check_ptr("logits", logits));
+    CHECK(check_ptr("idx", idx));
+    CHECK(check_ptr("w", w));
+    CHECK(check_rows("moe_router_topk_scores", T, H));
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, MOE_MAX_EXPERTS);
+    const int kmax = E < MOE_MAX_TOPK ? E : MOE_MAX_TOPK;
+    if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k=%d must be in [1, min(E, %d)=%d]", k, MOE_MAX_TOPK, kmax);
+    if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws) & 255u) return fail(MOE_EWORKSPACE, "workspace %p is not 256-byte aligned", ws);
+    if (ws_bytes < 256) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs 256", ws_bytes);
+    hipError_t e = launch_router((const uint16_t *)x, nullptr, 0.f, (const uint16_t *)router_w, T, H, E, k, nullptr,
+                                 logits, idx, w, (uint32_t *)ws + WS_ROUTER_ARRIVE, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_router_topk_scores launch", e);
+    return ok();
+}
+
+static size_t align256(size_t v) { return (v + 255u) & ~(size_t)255u; }
+
+static int validate_block(const moe_block *B) {
+    if (!B) return fail(MOE_EINVAL, "block descriptor is NULL");
+    CHECK(validate_layer(&B->layer));
+    CHECK(check_ptr("norm_gamma", B->norm_gamma));
+    CHECK(check_ptr("router_w", B->router_w));
+    if (!(B->norm_eps >= 0.f)) return fail(MOE_EINVAL, "norm_eps=%g must be >= 0", (double)B->norm_eps);
+    if (B->reserved != 0) return fail(MOE_EINVAL, "block reserved field must be 0");
+    return MOE_OK;
+}
+
+// block workspace: the layer's, then xn bf16 [T][H], then logits fp32 [T][E]
+static size_t block_xn_offset(const moe_block *B, int T) { return align256(ws_need(&B->layer, T)); }
+static size_t block_lg_offset(const moe_block *B, int T) {
+    return block_xn_offset(B, T) + align256((size_t)T * B->layer.hidden * 2);
+}
+static size_t block_ws_need(const moe_block *B, int T) {
+    return block_lg_offset(B, T) + align256((size_t)T * B->layer.n_experts * 4);
+}
+
+size_t moe_block_workspace_bytes(const moe_block *B, int T) {
+    if (validate_block(B) != MOE_OK) return 0;
+    if (T < 1 || T > MOE_MAX_TOKENS) {
+        fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+        return 0;
+    }
+    if (decode_supported(&B->layer, T) != MOE_OK) return 0;
+    ok();
+    return block_ws_need(B, T);
+}
+
+int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_t *idx_out, float *w_out, int flags,
+                     void *ws, size_t ws_bytes, void *stream) {
+    CHECK(validate_block(B));
+    const moe_layer *L = &B->layer;
+    if (T < 1 || T > MOE_MAX_TOKENS) return fail(MOE_EINVAL, "T=%d must be in [1, %d]", T, MOE_MAX_TOKENS);
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("out", out));
+    if (idx_out && !al16(idx_out)) return fail(MOE_EINVAL, "idx_out is not 16-byte aligned");
+    if (w_out && !al16(w_out)) return fail(MOE_EINVAL, "w_out is not 16-byte aligned");
+    CHECK(decode_supported(L, T));
+    if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)ws) & 255u) return fail(MOE_EWORKSPACE, "workspace %p is not 256-byte aligned", ws);
+    const size_t need = block_ws_need(B, T);
+    if (ws_bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    uint16_t *xn = (uint16_t *)((uint8_t *)ws + block_xn_offset(B, T));
+    float *lg = (float *)((uint8_t *)ws + block_lg_offset(B, T));
+    hipStream_t s = (hipStream_t)stream;
+    // norm + scores; the layer ranks them itself (top-k fused with the experts)
+    hipError_t e = launch_router((const uint16_t *)x, (const uint16_t *)B->norm_gamma, B->norm_eps,
+                                 (const uint16_t *)B->router_w, T, L->hidden, L->n_experts, L->top_k, xn, lg, nullptr,
+                                 nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail("moe_block_decode norm and scores launch", e);
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.L = layer_args(L);
+    a.x = xn;
+    a.logits = lg;
+    a.T = T;
+    a.out = out;
+    a.idx_out = idx_out;
+    a.w_out = w_out;
+    a.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+    a.mode = MODE_ROUTE;
+    a.ws = (uint8_t *)ws;
+    a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    a.residual = (const uint16_t *)x;
+    e = launch_layer(a, decoder_from_flags(flags), s);
+    if (e != hipSuccess) return hip_fail("moe_block_decode layer launch", e);
+    return ok();
+}
+
 int dense_gemv_q(const moe_qmat *W, const void *x, int B, void *y, int flags, void *stream) {
     if (!W) return fail(MOE_EINVAL, "matrix descriptor is NULL");
     if (!fmt_known(W->fmt)) return fail(MOE_EINVAL, "matrix fmt=%d is not a known format", W->fmt);

@@ -469,6 +469,8 @@ __device__ inline void route_one_token_wave(const float *__restrict__ logits, in
 
 __device__ inline float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+__device__ inline float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (u32)b << 16); }
+
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
     u32 u = __builtin_bit_cast(u32, f);
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN

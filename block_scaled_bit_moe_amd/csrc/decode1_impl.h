@@ -455,6 +455,7 @@ __global__ __launch_bounds__(D1_THREADS) void decode1_kernel(DecodeArgs a, D1Pla
 #pragma unroll 8
         for (int g = 0; g < k; ++g) acc = __builtin_fmaf(S.wsel[g], S.y[g * D1_MAX_RW + r], acc);
         if (Ish > 0) acc += S.y[k * D1_MAX_RW + r];
+        if (a.residual) acc += bf16_to_f32(a.residual[o0 + r]);
         if (a.out_f32) reinterpret_cast<float *>(a.out)[o0 + r] = acc;
         else reinterpret_cast<uint16_t *>(a.out)[o0 + r] = f32_to_bf16_rne(acc);
     }

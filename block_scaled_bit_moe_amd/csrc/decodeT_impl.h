@@ -591,6 +591,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                 }
             }
             const int64_t oi = (int64_t)t * H + o;
+            if (a.residual) acc += bf16_to_f32(a.residual[oi]);
             if (a.out_f32) reinterpret_cast<float *>(a.out)[oi] = acc;
             else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16_rne(acc);
         }

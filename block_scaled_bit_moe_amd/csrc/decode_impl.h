@@ -381,6 +381,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                                              acc);
                     if (add_shared) acc += __builtin_bit_cast(float, ld_relaxed_agent(ybuf + (size_t)S.pos_of[t][kk] * H + o));
                     const int64_t oi = (int64_t)t * H + o;
+                    if (a.residual) acc += bf16_to_f32(a.residual[oi]);
                     if (a.out_f32) reinterpret_cast<float *>(a.out)[oi] = acc;
                     else reinterpret_cast<uint16_t *>(a.out)[oi] = f32_to_bf16_rne(acc);
                 }

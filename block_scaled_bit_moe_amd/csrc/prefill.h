@@ -80,6 +80,7 @@ struct PfArgs {
     float *y;                 // [pairs][H] fp32
     void *out;                // [T][H] bf16 or fp32
     int out_f32;
+    const uint16_t *residual; // bf16 [T][H] of the chunk added before rounding (nullable)
     uint32_t *hdr;            // workspace header (arrival counter)
     int Imax;
 };
@@ -660,6 +661,13 @@ __global__ __launch_bounds__(PF_THREADS) void pf_combine_kernel(PfArgs a) {
             acc = *reinterpret_cast<const float4 *>(a.y + (size_t)s_p[0] * H + c);
         }
         const size_t o = (size_t)t * H + c;
+        if (a.residual) {
+            const uint2 r = *reinterpret_cast<const uint2 *>(a.residual + o);
+            acc.x += bf16_to_f32((uint16_t)(r.x & 0xFFFF));
+            acc.y += bf16_to_f32((uint16_t)(r.x >> 16));
+            acc.z += bf16_to_f32((uint16_t)(r.y & 0xFFFF));
+            acc.w += bf16_to_f32((uint16_t)(r.y >> 16));
+        }
         if (a.out_f32) {
             *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + o) = acc;
         } else {

@@ -94,6 +94,7 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
         p.y = (float *)(ws + l.y);
         p.out = (uint8_t *)a.out + (size_t)c0 * L.H * out_elt;
         p.out_f32 = a.out_f32;
+        p.residual = a.residual ? a.residual + (size_t)c0 * L.H : nullptr;
         p.hdr = (uint32_t *)ws;
         p.Imax = L.I > L.Ish ? L.I : L.Ish;
         if (a.mode == MODE_ROUTE) {

@@ -215,6 +215,51 @@ int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int
 int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *logits, int T, void *out,
                              int32_t *idx_out, float *w_out, int flags, void *stream);
 
+/* ---- The steps either side of the layer: the whole MoE block ----
+ * RMSNorm in front of the experts (nextsycl README, dense 27B engine: a norm
+ * that emits the next kernel's input; knivesysl README, "how it works": RMS
+ * fused into the quantisation), the router scores and their top-k as one
+ * launch (Strata docs/INTEL.md, "Decode round 2": scores + top-k fused to cut
+ * graph nodes), and the residual add after the layer.
+ *
+ * RMSNorm:  y[t][i] = x[t][i] * gamma[i] / sqrt(mean_j x[t][j]^2 + eps), in
+ * fp32 (sum of squares in a fixed order), one rounding to bf16 (or fp32 with
+ * MOE_OUT_F32).  x: device bf16 [T][H]; gamma: device bf16 [H]; y: [T][H].
+ * 1 <= T <= MOE_MAX_TOKENS, 32 <= H <= MOE_MAX_DIM, H a multiple of 32. */
+int moe_rmsnorm(const void *x, const void *gamma, int T, int H, float eps, void *y, int flags, void *stream);
+
+/* Router scores and top-k in one launch (T <= 16; two launches beyond):
+ *   logits[t][e] = sum_j router_w[e][j] * x[t][j]  (bf16 inputs, fp32 sums in
+ *   a fixed order), then idx/w as moe_route_topk of those scores.
+ * x: device bf16 [T][H]; router_w: device bf16 [E][H]; logits: device fp32
+ * [T][E]; idx int32 / w fp32 [T][k].  ws: device, >= 256 bytes, zeroed once
+ * (an arrival counter that the call returns to zero).  Limits as
+ * moe_route_topk; H as moe_rmsnorm. */
+int moe_router_topk_scores(const void *x, const void *router_w, int T, int H, int E, int k, float *logits,
+                           int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream);
+
+/* One MoE block: a layer plus the router and the norm in front of it. */
+typedef struct moe_block {
+    moe_layer layer;          /* the experts; hidden and n_experts also size the two arrays below */
+    const void *norm_gamma;   /* device bf16 [hidden]: RMSNorm gains */
+    const void *router_w;     /* device bf16 [n_experts][hidden]: router weights */
+    float norm_eps;           /* RMSNorm epsilon, >= 0 */
+    int32_t reserved;         /* must be 0 */
+} moe_block;
+
+/* Workspace of moe_block_decode for T tokens (0 when B or T breaks a rule):
+ * the layer's workspace followed by the normalised activation and the scores. */
+size_t moe_block_workspace_bytes(const moe_block *B, int T);
+
+/* The whole block on the residual stream x (bf16 [T][hidden]):
+ *   xn = bf16(RMSNorm(x)),  logits = router_w xn (fp32),
+ *   out = x + moe_layer(xn, logits)  (the residual added before the layer's
+ *   single rounding; bf16, or fp32 with MOE_OUT_F32).
+ * Two launches (norm + scores, then the layer with routing inside); idx_out /
+ * w_out as moe_layer_decode.  Other rules as moe_layer_decode. */
+int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_t *idx_out, float *w_out, int flags,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /* Dense block-scaled GEMV: y[b] = W x[b] for B tokens sharing every decoded
  * weight (knivesysl README, "formats": the fp6 projections).
  *   x: device bf16 [B][cols];  y: device [B][rows], bf16 or fp32 (MOE_OUT_F32)

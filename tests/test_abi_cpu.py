@@ -29,7 +29,9 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"moe_route_topk", "moe_layer_workspace_bytes", "moe_expert_ffn_q", "moe_layer_decode",
-                          "dense_gemv_q", "moe_last_error", "moe_version", "moe_workspace_status"}
+                          "dense_gemv_q", "moe_last_error", "moe_version", "moe_workspace_status",
+                          "moe_layer_decode_noalloc", "moe_rmsnorm", "moe_router_topk_scores",
+                          "moe_block_workspace_bytes", "moe_block_decode"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.moe_version() >= 100
@@ -160,3 +162,29 @@ def test_binding_refuses_cpu_tensors():
     logits = torch.zeros(1, 8)
     with pytest.raises(ValueError, match="GPU"):
         moeq.moe_route_topk(logits, 2)
+
+
+def test_block_steps_validation(lib):
+    """RMSNorm, router scores + top-k and the block refuse bad arguments before
+    anything is enqueued."""
+    assert lib.moe_rmsnorm(FAKE, FAKE, 1, 48, ctypes.c_float(1e-6), FAKE, 0, None) == moeq.MOE_EINVAL
+    assert "H=48" in _err(lib)
+    assert lib.moe_rmsnorm(FAKE, FAKE, 0, 64, ctypes.c_float(1e-6), FAKE, 0, None) == moeq.MOE_EINVAL
+    assert lib.moe_rmsnorm(FAKE, FAKE, 1, 64, ctypes.c_float(-1.0), FAKE, 0, None) == moeq.MOE_EINVAL
+    assert lib.moe_rmsnorm(FAKE, None, 1, 64, ctypes.c_float(1e-6), FAKE, 0, None) == moeq.MOE_EINVAL
+    ok = (FAKE, FAKE, 2, 64, 8, 2, FAKE, FAKE, FAKE)
+    assert lib.moe_router_topk_scores(*ok, None, 256, None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_router_topk_scores(*ok, FAKE2, 255, None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_router_topk_scores(FAKE, FAKE, 2, 64, 8, 9, FAKE, FAKE, FAKE, FAKE2, 256, None) == moeq.MOE_EINVAL
+    assert lib.moe_router_topk_scores(FAKE, FAKE, 2, 64, 1025, 2, FAKE, FAKE, FAKE, FAKE2, 256, None) == moeq.MOE_EINVAL
+    B = moeq.moe_block(_layer(), FAKE, FAKE, 1e-6, 0)
+    need = lib.moe_block_workspace_bytes(ctypes.byref(B), 4)
+    assert need > _ws_bytes(lib, _layer(), 4)
+    B.reserved = 1
+    assert lib.moe_block_workspace_bytes(ctypes.byref(B), 4) == 0 and "reserved" in _err(lib)
+    B.reserved, B.router_w = 0, None
+    assert lib.moe_block_workspace_bytes(ctypes.byref(B), 4) == 0 and "router_w" in _err(lib)
+    B.router_w = FAKE
+    assert lib.moe_block_decode(ctypes.byref(B), FAKE, 4, FAKE, None, None, 0, FAKE2, need - 1,
+                                None) == moeq.MOE_EWORKSPACE
+    assert lib.moe_block_decode(ctypes.byref(B), None, 4, FAKE, None, None, 0, FAKE2, need, None) == moeq.MOE_EINVAL
