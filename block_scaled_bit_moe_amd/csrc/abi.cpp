@@ -311,14 +311,15 @@ int moe_router_topk_scores(const void *x, const void *router_w, int T, int H, in
     CHECK(check_ptr("idx", idx));
     CHECK(check_ptr("w", w));
     CHECK(check_rows("moe_router_topk_scores", T, H));
+    if (H > ROUTER_MAX_H) return fail(MOE_EUNSUPPORTED, "H=%d above %d is not supported by the router kernel", H, ROUTER_MAX_H);
     if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "E=%d must be in [1, %d]", E, MOE_MAX_EXPERTS);
     const int kmax = E < MOE_MAX_TOPK ? E : MOE_MAX_TOPK;
     if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k=%d must be in [1, min(E, %d)=%d]", k, MOE_MAX_TOPK, kmax);
     if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
     if (((uintptr_t)ws) & 255u) return fail(MOE_EWORKSPACE, "workspace %p is not 256-byte aligned", ws);
     if (ws_bytes < 256) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs 256", ws_bytes);
-    hipError_t e = launch_router((const uint16_t *)x, nullptr, 0.f, (const uint16_t *)router_w, T, H, E, k, nullptr,
-                                 logits, idx, w, (uint32_t *)ws + WS_ROUTER_ARRIVE, (hipStream_t)stream);
+    hipError_t e = launch_router((const uint16_t *)x, (const uint16_t *)router_w, T, H, E, k, logits, idx, w,
+                                 (uint32_t *)ws + WS_ROUTER_ARRIVE, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_router_topk_scores launch", e);
     return ok();
 }
@@ -365,6 +366,8 @@ int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_
     if (idx_out && !al16(idx_out)) return fail(MOE_EINVAL, "idx_out is not 16-byte aligned");
     if (w_out && !al16(w_out)) return fail(MOE_EINVAL, "w_out is not 16-byte aligned");
     CHECK(decode_supported(L, T));
+    if (L->hidden > ROUTER_MAX_H)
+        return fail(MOE_EUNSUPPORTED, "hidden=%d above %d is not supported by the router kernel", L->hidden, ROUTER_MAX_H);
     if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL");
     if (((uintptr_t)ws) & 255u) return fail(MOE_EWORKSPACE, "workspace %p is not 256-byte aligned", ws);
     const size_t need = block_ws_need(B, T);
@@ -372,11 +375,13 @@ int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_
     uint16_t *xn = (uint16_t *)((uint8_t *)ws + block_xn_offset(B, T));
     float *lg = (float *)((uint8_t *)ws + block_lg_offset(B, T));
     hipStream_t s = (hipStream_t)stream;
-    // norm + scores; the layer ranks them itself (top-k fused with the experts)
-    hipError_t e = launch_router((const uint16_t *)x, (const uint16_t *)B->norm_gamma, B->norm_eps,
-                                 (const uint16_t *)B->router_w, T, L->hidden, L->n_experts, L->top_k, xn, lg, nullptr,
-                                 nullptr, nullptr, s);
-    if (e != hipSuccess) return hip_fail("moe_block_decode norm and scores launch", e);
+    // norm, then scores; the layer ranks them itself (top-k fused with the experts)
+    hipError_t e = launch_rmsnorm((const uint16_t *)x, (const uint16_t *)B->norm_gamma, T, L->hidden, B->norm_eps, xn,
+                                  0, s);
+    if (e != hipSuccess) return hip_fail("moe_block_decode norm launch", e);
+    e = launch_router(xn, (const uint16_t *)B->router_w, T, L->hidden, L->n_experts, L->top_k, lg, nullptr, nullptr,
+                      nullptr, s);
+    if (e != hipSuccess) return hip_fail("moe_block_decode scores launch", e);
     DecodeArgs a;
     memset(&a, 0, sizeof a);
     a.L = layer_args(L);

@@ -6,73 +6,96 @@
 // scores + top-k as one graph node), and the residual add, which the layer's
 // combine does before its single rounding.
 //
-// router_kernel: workgroup b computes the scores of router rows 4b .. 4b+3,
-// one row per wave, for every token.  The tokens' activations are staged in
-// LDS in batches; with NORM each workgroup normalises them itself (the same
-// arithmetic in every workgroup, so every copy is bitwise the same) and
-// workgroup 0 writes them out for the layer.  A row's 64 lanes take 16-byte
-// pieces of it, 4 bf16 pairs per token each (dot2, fp32), reduced in a fixed
-// order.  For up to 16 tokens the last workgroup to finish (an agent-scope
-// counter in the workspace header, reset by that workgroup) ranks the scores:
-// one wave per token, the routing of the decode kernels.
+// rmsnorm_kernel: one workgroup per token, its sum of squares in a fixed
+// order.  router_kernel: one workgroup per router row, the row's quarters on
+// the four waves, every token's score reduced in a fixed order; for up to 16
+// tokens the last workgroup to finish (an agent-scope counter in the
+// workspace header, reset by that workgroup) ranks the scores in the same
+// launch, one wave per token, with the routing of the decode kernels.
 #include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
+#include "memops.h"
 
 namespace moeq {
 
 constexpr int BK_THREADS = 256;
-constexpr int BK_MAX_TB = 16;                    // tokens per staged batch
-constexpr size_t BK_LDS = 64 * 1024;             // staged activations (bf16)
 
-// Sum over the 256 threads in a fixed order: each wave's DPP sum (valid in
-// every lane), then the four wave sums in order.
-__device__ inline float bk_block_sum(float v, float *s_tmp) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    v = group_sum_dpp(v, 64);
-    if (lane == 0) s_tmp[wv] = v;
-    __syncthreads();
-    const float r = ((s_tmp[0] + s_tmp[1]) + s_tmp[2]) + s_tmp[3];
-    __syncthreads();
-    return r;
+// One normalised bf16 pair: (x * g) * r, each product in fp32, one rounding.
+__device__ inline u32 bk_norm_pair(u32 x2, u32 g2, float r) {
+    const float x0 = __builtin_bit_cast(float, x2 << 16), x1 = __builtin_bit_cast(float, x2 & 0xFFFF0000u);
+    const float g0 = __builtin_bit_cast(float, g2 << 16), g1 = __builtin_bit_cast(float, g2 & 0xFFFF0000u);
+    return (u32)f32_to_bf16_rne((x0 * g0) * r) | ((u32)f32_to_bf16_rne((x1 * g1) * r) << 16);
 }
 
-// 1 / sqrt(mean of the squares of row x + eps), the mean in fp32 over the
-// 256 threads' partial sums (thread i sums elements i, i + 256, ... in order)
-__device__ inline float bk_inv_rms(const uint16_t *x, int H, float eps, float *s_tmp) {
-    float ss = 0.f;
-    for (int j = threadIdx.x; j < H; j += BK_THREADS) {
-        const float v = bf16_to_f32(x[j]);
-        ss = __builtin_fmaf(v, v, ss);
-    }
-    const float tot = bk_block_sum(ss, s_tmp);
-    return 1.0f / __builtin_sqrtf(tot / (float)H + eps);
-}
-
-// y = x * g * r for one row (bf16 out, or fp32)
+// y = x * g * r for one row per workgroup (bf16 out, or fp32).  A thread's
+// pieces of the row and of the gains are loaded together first (one round
+// trip), summed, then normalised from registers.
+constexpr int BK_NORM_MAXC = 16;   // pieces per thread: H <= 16 * 8 * 256
+template <int MC>
 __global__ __launch_bounds__(BK_THREADS) void rmsnorm_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ g, int H, float eps,
                                                             void *__restrict__ y, int out_f32) {
-    __shared__ float s_tmp[4];
+    __shared__ float s_tmp[1][4];
+    const int tid = threadIdx.x, nc = H / 8;
     const uint16_t *xt = x + (int64_t)blockIdx.x * H;
-    const float r = bk_inv_rms(xt, H, eps, s_tmp);
-    for (int j = threadIdx.x; j < H; j += BK_THREADS) {
-        const float v = (bf16_to_f32(xt[j]) * bf16_to_f32(g[j])) * r;
-        const int64_t o = (int64_t)blockIdx.x * H + j;
-        if (out_f32) reinterpret_cast<float *>(y)[o] = v;
-        else reinterpret_cast<uint16_t *>(y)[o] = f32_to_bf16_rne(v);
+    uint4 xq[MC], gq[MC];
+#pragma unroll
+    for (int i = 0; i < MC; ++i) {
+        const int c = min(tid + BK_THREADS * i, nc - 1);
+        xq[i] = *reinterpret_cast<const uint4 *>(xt + 8 * c);
+        gq[i] = *reinterpret_cast<const uint4 *>(g + 8 * c);
+    }
+    // sum of squares: each thread its pieces in order, then DPP, then the four waves in order
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MC; ++i) {
+        if (tid + BK_THREADS * i < nc) {
+            const u32 v4[4] = {xq[i].x, xq[i].y, xq[i].z, xq[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = __builtin_bit_cast(float, v4[j] << 16), hi = __builtin_bit_cast(float, v4[j] & 0xFFFF0000u);
+                ss = __builtin_fmaf(lo, lo, ss);
+                ss = __builtin_fmaf(hi, hi, ss);
+            }
+        }
+    }
+    const int lane = tid & 63, wv = tid >> 6;
+    const float wsum = group_sum_dpp(ss, 64);
+    if (lane == 0) s_tmp[0][wv] = wsum;
+    __syncthreads();
+    const float r = 1.0f / __builtin_sqrtf((((s_tmp[0][0] + s_tmp[0][1]) + s_tmp[0][2]) + s_tmp[0][3]) / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < MC; ++i) {
+        const int c = tid + BK_THREADS * i;
+        if (c >= nc) continue;
+        const u32 xv[4] = {xq[i].x, xq[i].y, xq[i].z, xq[i].w}, gv[4] = {gq[i].x, gq[i].y, gq[i].z, gq[i].w};
+        const int64_t o = (int64_t)blockIdx.x * H + 8 * c;
+        if (out_f32) {
+            float *yo = reinterpret_cast<float *>(y) + o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x0 = __builtin_bit_cast(float, xv[j] << 16), x1 = __builtin_bit_cast(float, xv[j] & 0xFFFF0000u);
+                const float g0 = __builtin_bit_cast(float, gv[j] << 16), g1 = __builtin_bit_cast(float, gv[j] & 0xFFFF0000u);
+                yo[2 * j] = (x0 * g0) * r;
+                yo[2 * j + 1] = (x1 * g1) * r;
+            }
+        } else {
+            uint4 q;
+            q.x = bk_norm_pair(xv[0], gv[0], r);
+            q.y = bk_norm_pair(xv[1], gv[1], r);
+            q.z = bk_norm_pair(xv[2], gv[2], r);
+            q.w = bk_norm_pair(xv[3], gv[3], r);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + o) = q;
+        }
     }
 }
 
 struct RouterArgs {
-    const uint16_t *x;        // bf16 [T][H]: the activation (NORM: the residual stream)
-    const uint16_t *gamma;    // bf16 [H] (NORM)
+    const uint16_t *x;        // bf16 [T][H]
     const uint16_t *wr;       // bf16 [E][H]
-    float eps;
     int T, H, E, k;
-    int tb;                   // tokens per staged batch
-    uint16_t *xn_out;         // bf16 [T][H] normalised activation (NORM; written by workgroup 0)
     float *logits;            // fp32 [T][E]
     int32_t *idx;             // [T][k] (fused top-k; nullable)
     float *w;                 // [T][k]
@@ -83,10 +106,16 @@ struct RouterArgs {
 template <int PER_LANE>
 __device__ inline void bk_route_tokens(const RouterArgs &a) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t lr = rsrc_of(a.logits, (uint64_t)a.T * a.E * 4);
     for (int t = wv; t < a.T; t += BK_THREADS / 64) {
         int e;
         float wt;
-        route_one_token_wave<PER_LANE>(a.logits + (int64_t)t * a.E, a.E, a.k, lane, e, wt);
+        float lg[PER_LANE];
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j)   // device-coherent loads (sc1) of the token's scores
+            lg[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  lr, (int)((t * a.E + min(lane * PER_LANE + j, a.E - 1)) * 4), 0, 16));
+        route_from_logits<PER_LANE>(lg, a.E, a.k, lane, e, wt);
         if (lane < a.k) {
             if (a.idx) a.idx[(int64_t)t * a.k + lane] = e;
             if (a.w) a.w[(int64_t)t * a.k + lane] = wt;
@@ -94,76 +123,77 @@ __device__ inline void bk_route_tokens(const RouterArgs &a) {
     }
 }
 
-template <bool NORM>
+constexpr int BK_TG = 4;      // tokens per group: their activation pieces are loaded together
+
+// Workgroup e computes router row e for every token: wave q takes the q-th
+// quarter of the row, each lane its 16-byte pieces there (all loaded at
+// once); tokens go in groups of four whose activation pieces are loaded
+// together; per token the lane sums are reduced by DPP within the wave and the
+// four quarter sums added in order.
+template <int BK_MAXC>   // 16-byte pieces of the row per lane (H <= 8 * 64 * 4 * BK_MAXC)
 __global__ __launch_bounds__(BK_THREADS) void router_kernel(RouterArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];   // [tb][H]
-    __shared__ float s_tmp[4];
+    __shared__ float s_part[4][BK_TG];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = a.H, E = a.E;
-    const int e = blockIdx.x * 4 + wv;
-    const uint16_t *wrow = a.wr + (int64_t)min(e, E - 1) * H;
-    for (int t0 = 0; t0 < a.T; t0 += a.tb) {
-        const int tb = min(a.tb, a.T - t0);
-        // stage the batch (16-byte pieces; H is a multiple of 32)
-        for (int q = tid; q < tb * (H / 8); q += BK_THREADS) {
-            const int t = q / (H / 8), c = q - t * (H / 8);
-            *reinterpret_cast<uint4 *>(s_x + t * H + 8 * c) =
-                *reinterpret_cast<const uint4 *>(a.x + (int64_t)(t0 + t) * H + 8 * c);
+    const int H = a.H, E = a.E, e = blockIdx.x;
+    const int nc = H / 8, nq = (nc + 3) / 4, c0 = wv * nq, c1 = min(nc, c0 + nq);
+    const uint16_t *wrow = a.wr + (int64_t)e * H;
+    const __amdgpu_buffer_rsrc_t lr = rsrc_of(a.logits, (uint64_t)a.T * E * 4);
+    uint4 wq[BK_MAXC];
+#pragma unroll
+    for (int i = 0; i < BK_MAXC; ++i) {
+        const int c = c0 + lane + 64 * i;
+        wq[i] = *reinterpret_cast<const uint4 *>(wrow + 8 * min(c, nc - 1));
+    }
+    for (int t0 = 0; t0 < a.T; t0 += BK_TG) {
+        const int tg = min(BK_TG, a.T - t0);
+        uint4 xq[BK_TG][BK_MAXC];
+#pragma unroll
+        for (int t = 0; t < BK_TG; ++t)
+#pragma unroll
+            for (int i = 0; i < BK_MAXC; ++i) {
+                const int c = c0 + lane + 64 * i;
+                xq[t][i] = *reinterpret_cast<const uint4 *>(a.x + (int64_t)min(t0 + t, a.T - 1) * H + 8 * min(c, nc - 1));
+            }
+        float acc[BK_TG];
+#pragma unroll
+        for (int t = 0; t < BK_TG; ++t) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < BK_MAXC; ++i) {
+                if (c0 + lane + 64 * i < c1) {
+                    s = dot2(wq[i].x, xq[t][i].x, s);
+                    s = dot2(wq[i].y, xq[t][i].y, s);
+                    s = dot2(wq[i].z, xq[t][i].z, s);
+                    s = dot2(wq[i].w, xq[t][i].w, s);
+                }
+            }
+            acc[t] = group_sum_dpp(s, 64);
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int t = 0; t < BK_TG; ++t) s_part[wv][t] = acc[t];
+        __syncthreads();
+        if (tid < tg) {
+            const float v = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+            // device-coherent store (sc1): the last workgroup may run on another XCD
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), lr, (int)(((t0 + tid) * E + e) * 4), 0, 16);
         }
         __syncthreads();
-        if (NORM) {
-            for (int t = 0; t < tb; ++t) {
-                uint16_t *row = s_x + t * H;
-                const float r = bk_inv_rms(row, H, a.eps, s_tmp);
-                for (int j = tid; j < H; j += BK_THREADS) {
-                    const uint16_t v = f32_to_bf16_rne((bf16_to_f32(row[j]) * bf16_to_f32(a.gamma[j])) * r);
-                    row[j] = v;
-                    if (blockIdx.x == 0 && a.xn_out) a.xn_out[(int64_t)(t0 + t) * H + j] = v;
-                }
-            }
-            __syncthreads();
-        }
-        // scores of row e for the batch: lane l takes the 16-byte pieces l, l + 64, ...
-        float acc[BK_MAX_TB];
-#pragma unroll
-        for (int t = 0; t < BK_MAX_TB; ++t) acc[t] = 0.f;
-        for (int c = lane; c < H / 8; c += 64) {
-            const uint4 wq = *reinterpret_cast<const uint4 *>(wrow + 8 * c);
-            const u32 wv4[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-            for (int t = 0; t < BK_MAX_TB; ++t) {
-                if (t < tb) {
-                    const uint4 xq = *reinterpret_cast<const uint4 *>(s_x + t * H + 8 * c);
-                    const u32 xv4[4] = {xq.x, xq.y, xq.z, xq.w};
-                    float s = acc[t];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s = dot2(wv4[i], xv4[i], s);
-                    acc[t] = s;
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < BK_MAX_TB; ++t) {
-            if (t < tb) {
-                const float v = group_sum_dpp(acc[t], 64);
-                if (lane == 0 && e < E) a.logits[(int64_t)(t0 + t) * E + e] = v;
-            }
-        }
-        __syncthreads();   // the batch's LDS is free
     }
     if (!a.fused) return;
-    // the last workgroup to finish ranks every token's scores
-    __threadfence();
+    // the last workgroup to finish ranks every token's scores: each workgroup's
+    // stores complete before its arrival is counted, and the last one reads
+    // the scores device-coherently
+    wait_vm<0>();
     __syncthreads();
     if (tid == 0) {
-        const u32 old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const u32 old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = old == gridDim.x - 1;
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     if (E <= 64) bk_route_tokens<1>(a);
     else if (E <= 128) bk_route_tokens<2>(a);
     else if (E <= 256) bk_route_tokens<4>(a);
@@ -174,38 +204,38 @@ __global__ __launch_bounds__(BK_THREADS) void router_kernel(RouterArgs a) {
 
 hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *g, int T, int H, float eps, void *y, int out_f32,
                           hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
+    const int mc = (H / 8 + BK_THREADS - 1) / BK_THREADS;
+    if (mc <= 1) hipLaunchKernelGGL(rmsnorm_kernel<1>, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
+    else if (mc <= 2) hipLaunchKernelGGL(rmsnorm_kernel<2>, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
+    else if (mc <= 4) hipLaunchKernelGGL(rmsnorm_kernel<4>, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
+    else if (mc <= 8) hipLaunchKernelGGL(rmsnorm_kernel<8>, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
+    else hipLaunchKernelGGL(rmsnorm_kernel<BK_NORM_MAXC>, dim3(T), dim3(BK_THREADS), 0, s, x, g, H, eps, y, out_f32);
     return hipGetLastError();
 }
 
-hipError_t launch_router(const uint16_t *x, const uint16_t *gamma, float eps, const uint16_t *wr, int T, int H, int E,
-                         int k, uint16_t *xn_out, float *logits, int32_t *idx, float *w, uint32_t *counter,
-                         hipStream_t s) {
+hipError_t launch_router(const uint16_t *x, const uint16_t *wr, int T, int H, int E, int k, float *logits,
+                         int32_t *idx, float *w, uint32_t *counter, hipStream_t s) {
+    if (H > ROUTER_MAX_H) return hipErrorInvalidValue;
     RouterArgs a;
     a.x = x;
-    a.gamma = gamma;
     a.wr = wr;
-    a.eps = eps;
     a.T = T;
     a.H = H;
     a.E = E;
     a.k = k;
-    a.tb = (int)std::min<size_t>(BK_MAX_TB, BK_LDS / ((size_t)H * 2));
-    a.xn_out = xn_out;
     a.logits = logits;
     a.idx = idx;
     a.w = w;
     a.counter = counter;
-    a.fused = (T <= BK_MAX_TB && (idx || w)) ? 1 : 0;
-    if (a.tb < 1) return hipErrorInvalidValue;
-    const size_t dyn = (size_t)a.tb * H * 2;
-    auto kern = gamma ? router_kernel<true> : router_kernel<false>;
-    const hipError_t le = ensure_dyn_lds(reinterpret_cast<const void *>(kern), dyn);
-    if (le != hipSuccess) return le;
-    hipLaunchKernelGGL(kern, dim3((E + 3) / 4), dim3(BK_THREADS), dyn, s, a);
+    a.fused = (T <= 16 && (idx || w)) ? 1 : 0;
+    const int per_lane = (H / 8 + 255) / 256;
+    if (per_lane <= 1) hipLaunchKernelGGL(router_kernel<1>, dim3(E), dim3(BK_THREADS), 0, s, a);
+    else if (per_lane <= 2) hipLaunchKernelGGL(router_kernel<2>, dim3(E), dim3(BK_THREADS), 0, s, a);
+    else if (per_lane <= 4) hipLaunchKernelGGL(router_kernel<4>, dim3(E), dim3(BK_THREADS), 0, s, a);
+    else hipLaunchKernelGGL(router_kernel<8>, dim3(E), dim3(BK_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.fused || !(idx || w)) return e;
-    // more tokens than one batch: rank in a launch of its own
+    // more than 16 tokens: rank in a launch of its own
     return launch_route(logits, T, E, k, idx, w, s);
 }
 

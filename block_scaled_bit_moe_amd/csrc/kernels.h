@@ -70,17 +70,16 @@ __host__ __device__ inline int down_lanes_per_row(int I, int Ish) {
 
 hipError_t launch_route(const float *logits, int T, int E, int k, int32_t *idx, float *w, hipStream_t s);
 
-// The steps either side of the layer (block.hip).  launch_router: scores of
-// router weights wr [E][H] (bf16) for T tokens; with gamma the tokens are the
-// residual stream and are RMS-normalised first (xn_out receives the bf16
-// normalised rows); with idx/w the top-k follows (in the same launch for
-// T <= 16, using the arrival counter, which must be zero between calls).
+// The steps either side of the layer (block.hip).  launch_rmsnorm: y = x g /
+// sqrt(mean x^2 + eps) per row.  launch_router: scores of router weights wr
+// [E][H] (bf16) for T tokens, then with idx/w the top-k (in the same launch
+// for T <= 16, using the arrival counter, which must be zero between calls).
 constexpr int WS_ROUTER_ARRIVE = 5;   // header word of that counter
+constexpr int ROUTER_MAX_H = 16384;   // hidden sizes the router kernel takes
 hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *g, int T, int H, float eps, void *y, int out_f32,
                           hipStream_t s);
-hipError_t launch_router(const uint16_t *x, const uint16_t *gamma, float eps, const uint16_t *wr, int T, int H, int E,
-                         int k, uint16_t *xn_out, float *logits, int32_t *idx, float *w, uint32_t *counter,
-                         hipStream_t s);
+hipError_t launch_router(const uint16_t *x, const uint16_t *wr, int T, int H, int E, int k, float *logits,
+                         int32_t *idx, float *w, uint32_t *counter, hipStream_t s);
 hipError_t launch_gemv(int fmt, int dec, const uint8_t *codes, const uint8_t *scales, int rows, int cols,
                        const uint16_t *x, int B, void *y, int out_f32, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int dec, hipStream_t s);

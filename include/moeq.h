@@ -234,7 +234,7 @@ int moe_rmsnorm(const void *x, const void *gamma, int T, int H, float eps, void 
  * x: device bf16 [T][H]; router_w: device bf16 [E][H]; logits: device fp32
  * [T][E]; idx int32 / w fp32 [T][k].  ws: device, >= 256 bytes, zeroed once
  * (an arrival counter that the call returns to zero).  Limits as
- * moe_route_topk; H as moe_rmsnorm. */
+ * moe_route_topk; H as moe_rmsnorm and at most 16384. */
 int moe_router_topk_scores(const void *x, const void *router_w, int T, int H, int E, int k, float *logits,
                            int32_t *idx, float *w, void *ws, size_t ws_bytes, void *stream);
 
@@ -255,8 +255,9 @@ size_t moe_block_workspace_bytes(const moe_block *B, int T);
  *   xn = bf16(RMSNorm(x)),  logits = router_w xn (fp32),
  *   out = x + moe_layer(xn, logits)  (the residual added before the layer's
  *   single rounding; bf16, or fp32 with MOE_OUT_F32).
- * Two launches (norm + scores, then the layer with routing inside); idx_out /
- * w_out as moe_layer_decode.  Other rules as moe_layer_decode. */
+ * Three launches (the norm, the scores, then the layer, which ranks the
+ * scores itself: top-k fused with the experts); idx_out / w_out as
+ * moe_layer_decode.  hidden <= 16384.  Other rules as moe_layer_decode. */
 int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_t *idx_out, float *w_out, int flags,
                      void *ws, size_t ws_bytes, void *stream);
 
