@@ -57,6 +57,7 @@ def _load():
     lib.oracle_rmsnorm.argtypes = [i64, i64, vp, vp, ctypes.c_double, vp]
     lib.oracle_router_logits.argtypes = [i64, i64, i64, vp, vp, vp]
     lib.oracle_residual_add.argtypes = [i64, vp, vp, vp]
+    lib.oracle_quantize_mx_e4m3.argtypes = [i64, i64, vp, vp, vp]
     lib.oracle_threads.argtypes = [i32]
     lib.oracle_threads.restype = i32
     lib.oracle_init()
@@ -259,6 +260,25 @@ def block(fmt, H, I, E, k, experts, x_bf16, gamma_bf16, wr_bf16, eps, shared=Non
                       shared_inter=shared_inter, out_rows=out_rows)
     r = x if out_rows is None else x[:, np.asarray(out_rows)]
     return idx, w, residual_add(np.ascontiguousarray(r), y), xn, lg
+
+
+def quantize_mx_e4m3(x_bf16):
+    """Activations [T][H] (bf16 bits) -> (e4m3 codes uint8 [T][H], UE8M0 scales uint8 [T][H/32])."""
+    x, px = _c(np.atleast_2d(x_bf16), np.uint16)
+    T, H = x.shape
+    assert H % 32 == 0
+    codes = np.empty((T, H), np.uint8)
+    scales = np.empty((T, H // 32), np.uint8)
+    _load().oracle_quantize_mx_e4m3(T, H, px, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def dequantize_mx_e4m3(codes, scales):
+    """value(code) * 2^(scale - 127) in double."""
+    t = tables()
+    c = np.asarray(codes)
+    s = np.repeat(np.asarray(scales).astype(np.float64) - 127.0, 32, axis=-1)
+    return t["e4m3"][c] * np.exp2(s)
 
 
 def use_library(path=None):

@@ -357,6 +357,53 @@ void oracle_residual_add(int64_t n, const uint16_t *r, const double *y, double *
     for (int64_t i = 0; i < n; ++i) out[i] = bf16_value(r[i]) + y[i];
 }
 
+/* ---- Activation quantisation for the scaled matrix cores (the pages' fp6
+ * path with e4m3 activations: knivesysl README, "formats" and "key flags";
+ * amax scaling as in Strata docs/INTEL.md, "The engine itself on Intel",
+ * whose activation quantiser is byte-exact to its reference).  MX element
+ * format e4m3 with a UE8M0 scale per block of 32 consecutive elements of a
+ * row, by the OCP MX rule:
+ *   amax = max |x| over the block;
+ *   scale exponent X = floor(log2(amax)) - 8 (8: the largest binade of e4m3,
+ *   whose largest value is 448 = 1.75 * 2^8), clamped to [-127, 127]; a block
+ *   of zeros takes X = -127;
+ *   each element: x / 2^X rounded to the nearest e4m3 value, ties to the even
+ *   code, magnitudes above 448 saturated to 448; the sign kept (-0 too).
+ * The dequantised element is value(code) * 2^X. */
+
+/* The e4m3 code nearest to v (ties to the even code), saturating at 448. */
+static uint8_t e4m3_nearest(double v) {
+    const uint8_t s = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    unsigned best = 0;
+    double bd = INFINITY;
+    for (unsigned c = 0; c < 0x7F; ++c) {           /* the 127 finite non-negative codes, in value order */
+        const double d = fabs(T_E4M3[c] - a);
+        if (d < bd || (d == bd && (c & 1u) == 0)) { bd = d; best = c; }
+    }
+    return (uint8_t)(s | best);
+}
+
+void oracle_quantize_mx_e4m3(int64_t T, int64_t H, const uint16_t *x, uint8_t *codes, uint8_t *scales) {
+    build_tables();
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t b = 0; b < H / 32; ++b) {
+            const uint16_t *xb = x + t * H + 32 * b;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs(bf16_value(xb[j])));
+            int X = -127;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e);                     /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+                X = (e - 1) - 8;
+                if (X < -127) X = -127;
+                if (X > 127) X = 127;
+            }
+            scales[t * (H / 32) + b] = (uint8_t)(X + 127);
+            for (int j = 0; j < 32; ++j) codes[t * H + 32 * b + j] = e4m3_nearest(ldexp(bf16_value(xb[j]), -X));
+        }
+}
+
 /* Round a double to bfloat16, once, to nearest with ties to even.  Rounding
  * works on the significand scaled to eight bits (normal range) or on the
  * fixed unit 2^-133 (subnormal range). */

@@ -44,6 +44,11 @@ MUTANTS = {
     "rmsnorm_no_gain": ("y[t * H + i] = bf16_value(xt[i]) * bf16_value(g[i]) * r;", "y[t * H + i] = bf16_value(xt[i]) * r;"),
     "router_transposed": ("bf16_value(wr[e * H + j])", "bf16_value(wr[j * E + e])"),
     "residual_dropped": ("out[i] = bf16_value(r[i]) + y[i];", "out[i] = y[i];"),
+    "quant_emax": ("X = (e - 1) - 8;", "X = (e - 1) - 7;"),
+    "quant_ceil": ("X = (e - 1) - 8;", "X = e - 8;"),
+    "quant_ties_odd": ("(d == bd && (c & 1u) == 0)", "(d == bd && (c & 1u) == 1)"),
+    "quant_block16": ("const uint16_t *xb = x + t * H + 32 * b;", "const uint16_t *xb = x + t * H + 16 * b;"),
+    "quant_sign_dropped": ("const uint8_t s = signbit(v) ? 0x80 : 0x00;", "const uint8_t s = 0x00;"),
     "e2m3_e4m3_block": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_E4M3[srow[j / 128]]"),
     "e2m3_e4m3_scale_kind": ("T_E2M3[c] * T_E4M3[srow[j / 16]]", "T_E2M3[c] * T_UE8M0[srow[j / 16]]"),
     "ue8m0_bias": ("ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 126)"),
@@ -219,8 +224,29 @@ def _pin_block():
     assert list(oracle.residual_add(np.array([0x3FC0, 0xC000], np.uint16), np.array([0.25, 0.5]))) == [1.75, -1.5]
 
 
+def _pin_quant():
+    """Quantiser: a power-of-two block, saturation, -0, and torch's e4m3
+    rounding of a scaled random block."""
+    x = np.full((1, 32), 0x4080, np.uint16)                       # 4.0
+    c, s = oracle.quantize_mx_e4m3(x)
+    assert s[0, 0] == 127 + 2 - 8 and (c == 0x78).all()
+    xs = np.full((1, 32), 0x3F00, np.uint16)                      # 0.5
+    xs[0, 0], xs[0, 1], xs[0, 2] = 0x40F8, 0xC0F8, 0x8000         # 7.75, -7.75, -0
+    c, s = oracle.quantize_mx_e4m3(xs)
+    assert s[0, 0] == 127 + 2 - 8 and c[0, 0] == 0x7E and c[0, 1] == 0xFE and c[0, 2] == 0x80
+    import torch
+    cfg = MoEConfig("q", tokens=2, hidden=64, experts=2, top_k=1, inter=32, x_sigma=3.0)
+    xr = synth.hidden_states(cfg)
+    c, s = oracle.quantize_mx_e4m3(xr)
+    xf = (xr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sc = xf / np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    ok = np.abs(sc) <= 448
+    assert np.array_equal(c[ok], torch.from_numpy(sc[ok]).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(s.astype(np.float64) - 127, np.floor(np.log2(np.abs(xf).reshape(2, 2, 32).max(axis=2))) - 8)
+
+
 PINS = [_pin_tables, _pin_packing, _pin_scale_blocks, _pin_gemv, _pin_route, _pin_silu, _pin_ffn_and_layer,
-        _pin_formats, _pin_block]
+        _pin_formats, _pin_block, _pin_quant]
 
 
 def _failures():
