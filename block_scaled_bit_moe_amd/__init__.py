@@ -8,6 +8,7 @@ not on the GPU, the call raises.
 Functions carry the C names: moe_route_topk, moe_layer_workspace_bytes,
 moe_expert_ffn_q, moe_layer_decode, moe_layer_decode_noalloc, dense_gemv_q,
 moe_rmsnorm, moe_router_topk_scores, moe_block_workspace_bytes, moe_block_decode,
+moe_quantize_mx_e4m3,
 moe_workspace_status, moe_last_error, moe_version.
 """
 import ctypes
@@ -23,6 +24,7 @@ MOE_FMT_E2M1_E4M3_B16, MOE_FMT_E2M3_UE8M0_B128 = 1, 2
 MOE_FMT_E2M1_UE8M0_B32, MOE_FMT_INT4_F16_B64, MOE_FMT_E2M3_E4M3_B16 = 3, 4, 5
 FORMATS = (1, 2, 3, 4, 5)
 MOE_OUT_F32 = 1
+MOE_ACT_MXFP8 = 1 << 27
 MOE_DECODER_LUT = 1 << 28
 MOE_DECODER_HW = 1 << 29
 MOE_DEBUG_SPIN_LIMIT = 1 << 30
@@ -74,6 +76,7 @@ def load_library(path=None):
     lib.moe_layer_decode_noalloc.argtypes = [ctypes.POINTER(moe_layer), vp, vp, i32, vp, vp, vp, i32, vp]
     lib.dense_gemv_q.argtypes = [ctypes.POINTER(moe_qmat), vp, i32, vp, i32, vp]
     lib.moe_rmsnorm.argtypes = [vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]
+    lib.moe_quantize_mx_e4m3.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_router_topk_scores.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_block_workspace_bytes.argtypes = [ctypes.POINTER(moe_block), i32]
     lib.moe_block_workspace_bytes.restype = sz
@@ -83,7 +86,8 @@ def load_library(path=None):
     lib.moe_last_error.argtypes = []
     lib.moe_version.restype = i32
     for f in ("moe_route_topk", "moe_expert_ffn_q", "moe_layer_decode", "moe_layer_decode_noalloc", "dense_gemv_q",
-              "moe_workspace_status", "moe_rmsnorm", "moe_router_topk_scores", "moe_block_decode"):
+              "moe_workspace_status", "moe_rmsnorm", "moe_router_topk_scores", "moe_block_decode",
+              "moe_quantize_mx_e4m3"):
         getattr(lib, f).restype = i32
     if path is None:
         _lib = lib
@@ -306,6 +310,18 @@ def moe_rmsnorm(x, gamma, eps, y=None, flags=0):
     _check(load_library().moe_rmsnorm(_dev(x, "x", _BF16), _dev(gamma, "gamma", _BF16), T, H, float(eps),
                                       _dev(y, "y", (torch.bfloat16, torch.float32)), flags, _stream()))
     return y
+
+
+def moe_quantize_mx_e4m3(x, codes=None, scales=None):
+    """x bf16 [T][H] -> (MX e4m3 codes uint8 [T][H], UE8M0 scales uint8 [T][H/32])."""
+    T, H = x.shape
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device) if codes is None else codes
+    scales = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device) if scales is None else scales
+    _shape(codes, "codes", (T, H))
+    _shape(scales, "scales", (T, H // 32))
+    _check(load_library().moe_quantize_mx_e4m3(_dev(x, "x", _BF16), T, H, _dev(codes, "codes", _U8),
+                                               _dev(scales, "scales", _U8), _stream()))
+    return codes, scales
 
 
 def moe_router_topk_scores(x, router_w, k, logits=None, idx=None, w=None, ws=None):

@@ -210,6 +210,7 @@ int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void 
     a.fixed_e = expert;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    a.act_mx = (flags & MOE_ACT_MXFP8) ? 1 : 0;
     hipError_t e = launch_layer(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_expert_ffn_q launch", e);
     return ok();
@@ -240,6 +241,7 @@ int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int
     a.fixed_e = 0;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    a.act_mx = (flags & MOE_ACT_MXFP8) ? 1 : 0;
     hipError_t e = launch_layer(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_layer_decode launch", e);
     return ok();
@@ -279,6 +281,7 @@ int moe_layer_decode_noalloc(const moe_layer *L, const void *x, const float *log
     a.fixed_e = 0;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    a.act_mx = (flags & MOE_ACT_MXFP8) ? 1 : 0;
     e = launch_decode(a, decoder_from_flags(flags), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("moe_layer_decode_noalloc launch", e);
     return ok();
@@ -395,9 +398,21 @@ int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_
     a.mode = MODE_ROUTE;
     a.ws = (uint8_t *)ws;
     a.spin_limit = (flags & MOE_DEBUG_SPIN_LIMIT) ? 0u : (1u << 20);
+    a.act_mx = (flags & MOE_ACT_MXFP8) ? 1 : 0;
     a.residual = (const uint16_t *)x;
     e = launch_layer(a, decoder_from_flags(flags), s);
     if (e != hipSuccess) return hip_fail("moe_block_decode layer launch", e);
+    return ok();
+}
+
+int moe_quantize_mx_e4m3(const void *x, int T, int H, void *codes, void *scales, void *stream) {
+    CHECK(check_ptr("x", x));
+    CHECK(check_ptr("codes", codes));
+    CHECK(check_ptr("scales", scales));
+    CHECK(check_rows("moe_quantize_mx_e4m3", T, H));
+    hipError_t e = launch_mx_quant((const uint16_t *)x, T, H, (uint8_t *)codes, (uint8_t *)scales, nullptr,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("moe_quantize_mx_e4m3 launch", e);
     return ok();
 }
 

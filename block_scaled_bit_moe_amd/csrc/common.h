@@ -31,6 +31,7 @@ typedef uint32_t u32;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(6))) u32 u32x6_t;
 typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32_t;
+typedef __attribute__((ext_vector_type(2))) float f2_t;
 
 constexpr int FMT_E2M1 = 1;     // e2m1 + e4m3 per 16
 constexpr int FMT_E2M3 = 2;     // e2m3 + UE8M0 per 128

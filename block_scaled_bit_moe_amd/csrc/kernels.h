@@ -34,7 +34,18 @@ struct DecodeArgs {
     uint8_t *ws;
     uint32_t spin_limit;
     const uint16_t *residual;   // bf16 [T][H] added to the output before its rounding (nullable)
+    int act_mx;                 // quantise the activations to MX e4m3 (per 32) before gate | up
 };
+
+// Activation quantisation (quant.hip): bf16 [T][H] -> MX e4m3 codes [T][H]
+// and UE8M0 scales [T][H/32]; deq (nullable) receives the dequantised bf16.
+hipError_t launch_mx_quant(const uint16_t *x, int T, int H, uint8_t *codes, uint8_t *scales, uint16_t *deq,
+                           hipStream_t s);
+// Workspace bytes of that region for T tokens: codes, scales, dequantised rows.
+inline size_t act_quant_bytes(int T, int H) {
+    auto al = [](size_t v) { return (v + 255u) & ~(size_t)255u; };
+    return al((size_t)T * H) + al((size_t)T * H / 32) + al((size_t)T * H * 2);
+}
 
 // decode-path workspace: header (counters, error word) + h (hi/lo bf16) + y partials
 constexpr size_t WS_HEADER = 16384;
@@ -52,6 +63,7 @@ constexpr int DEC_S1 = 16;         // I-rows (gate and up) per gate/up item
 constexpr int DEC_S2 = 64;         // output rows per down item
 
 size_t decode_workspace_bytes(int T, int H, int I, int Ish, int k);
+size_t decode_quant_offset(int H, int I, int Ish);
 
 // Many-token path (T > DEC_MAX_T): tokens are processed in chunks of PF_CHUNK.
 constexpr int PF_CHUNK = 2048;

@@ -45,7 +45,6 @@ namespace moeq {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4_t;
-typedef __attribute__((ext_vector_type(2))) float f2_t;
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_MB = 64;                   // tokens per block (four 16-row sub-tiles)
@@ -83,6 +82,8 @@ struct PfArgs {
     const uint16_t *residual; // bf16 [T][H] of the chunk added before rounding (nullable)
     uint32_t *hdr;            // workspace header (arrival counter)
     int Imax;
+    const uint8_t *xq;        // MX e4m3 activations [T][H] of the chunk (scaled matrix cores; nullable)
+    const uint8_t *xs;        // their UE8M0 scales [T][H/32]
 };
 
 constexpr int WS_PF_ARRIVE = 4;   // header word: group workgroups finished
@@ -612,6 +613,146 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
         case 2: pf_gemm_main<FMT, DOWN, 2, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
         case 3: pf_gemm_main<FMT, DOWN, 3, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
         default: pf_gemm_main<FMT, DOWN, 4, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+    }
+}
+
+// Gate | up on the scaled matrix cores for the MX weight formats (e2m1 or
+// e2m3 codes with UE8M0 scales per 32, or per 128 = four blocks of 32 with one
+// byte) and MX e4m3 activations (scale per 32): v_mfma_scale_f32_16x16x128_f8f6f4
+// with the activations as A (16 tokens) and the weights as B (16 rows).  The
+// operand layout of that instruction, measured on this part with one-hot and
+// random operands: B lane group h holds K 32h .. 32h+31 of its column; A lane
+// group g holds K 16g .. 16g+15 in its first 16 bytes and 64+16g .. 64+16g+15
+// in its last 16; the scale of K block b (K 32b .. 32b+31) is lane group b's
+// scale byte, for A and for B alike, whichever lanes hold that block's data.
+// So for the 128-wide K step s, B lane group h loads weight unit 4s + h with
+// its scale, and A lane group g loads its two 16-byte pieces of the token's
+// codes and the scale of activation block 4s + g: one instruction per step.
+// One workgroup per (block of 64 tokens, tile of 64 intermediate rows), four
+// waves of 16 gate and the same 16 up rows; the next K step's loads are issued
+// before this step's MFMAs.  The epilogue is the bf16 path's: h = silu(g) * u
+// as a bf16 hi + lo pair.
+typedef __attribute__((ext_vector_type(8))) int v8i_t;
+
+template <int FMT>
+__device__ inline v8i_t pf_mx_b(const Unit<FMT> &U) {
+    v8i_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (!Fmt<FMT>::SIX) {
+        v[0] = (int)U.c.x; v[1] = (int)U.c.y; v[2] = (int)U.c.z; v[3] = (int)U.c.w;
+    } else {
+        v[0] = (int)U.c0.x; v[1] = (int)U.c0.y; v[2] = (int)U.c1.x; v[3] = (int)U.c1.y; v[4] = (int)U.c2.x;
+        v[5] = (int)U.c2.y;
+    }
+    return v;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void pf_gateup_mx_kernel(PfArgs a, int NT) {
+    static_assert(Fmt<FMT>::SCALE == SC_UE8M0, "MX weight formats only");
+    constexpr int BFMT = Fmt<FMT>::SIX ? 2 : 4;        // fp6 e2m3 or fp4 e2m1 operand
+    __shared__ int s_tok[PF_MB];
+    const int wid = blockIdx.x;
+    const int win = wid / (8 * NT), q = wid - win * 8 * NT;
+    const int b = win * 8 + (q & 7), nt = q >> 3;
+    if (b >= a.nblk[0]) return;
+    const int packed = a.blk[b];
+    const int slot = packed >> 16, m0 = packed & 0xFFFF;
+    const int E = a.L.E, H = a.L.H;
+    const bool shared = slot == E;
+    const int Is = shared ? a.L.Ish : a.L.I;
+    const int n0 = nt * 64;
+    if (n0 >= Is) return;
+    const int M = min(PF_MB, a.cnt[slot] - m0);
+    const int p0 = a.off[slot] + m0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    if (tid < PF_MB) s_tok[tid] = a.tok[(size_t)slot * a.T + m0 + min(tid, M - 1)];
+    __syncthreads();
+
+    using F = Fmt<FMT>;
+    const int64_t crb = F::code_row_bytes(H), srb = F::scale_row_bytes(H);
+    const uint8_t *wc = shared ? a.L.sh13c : a.L.w13c + (size_t)slot * 2 * Is * crb;
+    const uint8_t *ws = shared ? a.L.sh13s : a.L.w13s + (size_t)slot * 2 * Is * srb;
+    const int n = min(n0 + wv * 16 + lr, Is - 1);     // rows past Is: a valid row, result dropped
+    const uint8_t *rc[2] = {wc + (size_t)n * crb, wc + (size_t)(Is + n) * crb};
+    const uint8_t *rs[2] = {ws + (size_t)n * srb, ws + (size_t)(Is + n) * srb};
+    const int UK = H / 32, nK = (H + 127) / 128, HB = H / 32;
+    const uint8_t *arow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) arow[m] = a.xq + (size_t)s_tok[min(16 * m + lr, M - 1)] * H;
+    const uint8_t *srow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) srow[m] = a.xs + (size_t)s_tok[min(16 * m + lr, M - 1)] * HB;
+    const int nsub = (M + 15) >> 4;
+
+    Unit<FMT> wu[2][2];
+    uint4 ax[2][4][2];
+    u32 as[2][4];
+    auto load = [&](int st, int j) {
+        const int u = min(j * 4 + lg, UK - 1);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) load_unit<FMT>(wu[st][g], rc[g], rs[g], u);
+        // the two activation pieces, K 128 j + 16 lg and 128 j + 64 + 16 lg (kept inside the row)
+        const int k0 = min(128 * j + 16 * lg, H - 16), k1 = min(128 * j + 64 + 16 * lg, H - 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            ax[st][m][0] = *reinterpret_cast<const uint4 *>(arow[m] + k0);
+            ax[st][m][1] = *reinterpret_cast<const uint4 *>(arow[m] + k1);
+            as[st][m] = srow[m][u];
+        }
+    };
+    f32x4_t acc[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int st, int j) {
+        // K blocks past the row's end: weights 0 with unit scales, so they add exactly 0
+        const bool live = j * 4 + lg < UK;
+        v8i_t bw[2];
+        int bs[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            bw[g] = live ? pf_mx_b<FMT>(wu[st][g]) : v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+            bs[g] = live ? (int)(wu[st][g].s & 0xFF) : 127;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if (m < nsub) {
+                const v8i_t av = {(int)ax[st][m][0].x, (int)ax[st][m][0].y, (int)ax[st][m][0].z, (int)ax[st][m][0].w,
+                                  (int)ax[st][m][1].x, (int)ax[st][m][1].y, (int)ax[st][m][1].z, (int)ax[st][m][1].w};
+                const int sa = live ? (int)as[st][m] : 127;
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    acc[g][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[g], acc[g][m], 0, BFMT, 0, sa, 0,
+                                                                                 bs[g]);
+            }
+        }
+    };
+    load(0, 0);
+    for (int j = 0; j < nK; j += 2) {
+        load(1, j + 1);
+        step(0, j);
+        if (j + 1 >= nK) break;
+        load(0, j + 2);
+        step(1, j + 1);
+    }
+    // epilogue: lane holds tokens 16m + 4 lg + i, weight row n0 + 16 wv + lr
+    const int nn = n0 + wv * 16 + lr;
+    if (nn >= Is) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * m + 4 * lg + i;
+            if (t >= M) continue;
+            const size_t p = (size_t)(p0 + t);
+            const float h = silu_f32(acc[0][m][i]) * acc[1][m][i];
+            const uint16_t hi = f32_to_bf16_rne(h);
+            const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
+            a.h_hi[p * a.Imax + nn] = hi;
+            a.h_lo[p * a.Imax + nn] = lo;
+        }
     }
 }
 

@@ -6,7 +6,7 @@ namespace moeq {
 
 // Workspace of one chunk of Tc tokens, after the shared header.
 struct PfLayout {
-    size_t idx, w, rank, cnt, off, nblk, blk, tok, h_hi, h_lo, y, total;
+    size_t idx, w, rank, cnt, off, nblk, blk, tok, h_hi, h_lo, y, xq, xs, xd, total;
     int Tc, NS, pairs, nblk_max;
 };
 
@@ -44,6 +44,9 @@ static PfLayout pf_layout(int T, int H, int I, int Ish, int k, int E) {
     l.h_hi = take((size_t)l.pairs * Imax * 2);
     l.h_lo = take((size_t)l.pairs * Imax * 2);
     l.y = take((size_t)l.pairs * H * 4);
+    l.xq = take((size_t)l.Tc * H);          // MX activations of the chunk (MOE_ACT_MXFP8)
+    l.xs = take((size_t)l.Tc * H / 32);
+    l.xd = take((size_t)l.Tc * H * 2);
     l.total = o;
     return l;
 }
@@ -59,7 +62,15 @@ static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     const int nt_gu = (Imax + rows_gu - 1) / rows_gu;
     const int nt_dn = (p.L.H + rows_dn - 1) / rows_dn;
     hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
+    if constexpr (Fmt<FMT>::SCALE == SC_UE8M0) {
+        if (p.xq) {   // MX activations and MX weights: the scaled matrix cores
+            hipLaunchKernelGGL((pf_gateup_mx_kernel<FMT>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
+        } else {
+            hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
+        }
+    } else {
+        hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
+    }
     hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
     hipLaunchKernelGGL(pf_combine_kernel, dim3(p.T), dim3(PF_THREADS), 0, s, p);
     return hipGetLastError();
@@ -97,6 +108,22 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
         p.residual = a.residual ? a.residual + (size_t)c0 * L.H : nullptr;
         p.hdr = (uint32_t *)ws;
         p.Imax = L.I > L.Ish ? L.I : L.Ish;
+        p.xq = nullptr;
+        p.xs = nullptr;
+        if (a.act_mx) {
+            // the chunk's activations to MX e4m3; MX weights take the codes on the
+            // scaled matrix cores, the other formats the dequantised bf16 rows
+            const bool mx = L.fmt == FMT_E2M3 || L.fmt == FMT_MXFP4;
+            uint16_t *xd = (uint16_t *)(ws + l.xd);
+            hipError_t e = launch_mx_quant(p.x, Tc, L.H, ws + l.xq, ws + l.xs, mx ? nullptr : xd, s);
+            if (e != hipSuccess) return e;
+            if (mx) {
+                p.xq = ws + l.xq;
+                p.xs = ws + l.xs;
+            } else {
+                p.x = xd;
+            }
+        }
         if (a.mode == MODE_ROUTE) {
             hipError_t e = launch_route(a.logits + (size_t)c0 * L.E, Tc, L.E, L.k, idx, w, s);
             if (e != hipSuccess) return e;

@@ -111,6 +111,12 @@ enum {
 /* Flags. */
 enum {
     MOE_OUT_F32 = 1,        /* write the output as fp32 (the value before bf16 rounding) */
+    MOE_ACT_MXFP8 = 1 << 27,    /* quantise the activations entering gate | up to MX e4m3 with a
+                                   UE8M0 scale per 32 (moe_quantize_mx_e4m3) and use the quantised
+                                   values: with MX weights (formats 2 and 3) the many-token path
+                                   then runs gate | up on the scaled low-precision matrix cores;
+                                   every other path runs on the dequantised values, which bf16
+                                   holds exactly for activations in its normal range */
     MOE_DECODER_LUT = 1 << 28,  /* decode codes through byte-indexed tables in LDS */
     MOE_DECODER_HW = 1 << 29,   /* decode codes with gfx950's fp4/fp6 -> bf16 conversions
                                    (both decoders are exact and give identical results; with
@@ -260,6 +266,17 @@ size_t moe_block_workspace_bytes(const moe_block *B, int T);
  * moe_layer_decode.  hidden <= 16384.  Other rules as moe_layer_decode. */
 int moe_block_decode(const moe_block *B, const void *x, int T, void *out, int32_t *idx_out, float *w_out, int flags,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* Activation quantisation for the scaled matrix cores (the pages' fp6 path
+ * with e4m3 activations: knivesysl README, "formats" and "key flags"; an amax
+ * quantiser as Strata docs/INTEL.md, "The engine itself on Intel"): each
+ * block of 32 consecutive elements of a row gets the UE8M0 scale 2^X with
+ * X = floor(log2(max |x|)) - 8, clamped to [-127, 127] (-127 for a block of
+ * zeros), and each element the e4m3 code nearest to x / 2^X (ties to even,
+ * magnitudes past 448 saturated, sign kept).
+ *   x: device bf16 [T][H], H a multiple of 32;  codes: device u8 [T][H];
+ *   scales: device u8 [T][H/32]. */
+int moe_quantize_mx_e4m3(const void *x, int T, int H, void *codes, void *scales, void *stream);
 
 /* Dense block-scaled GEMV: y[b] = W x[b] for B tokens sharing every decoded
  * weight (knivesysl README, "formats": the fp6 projections).

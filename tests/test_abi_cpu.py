@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"moe_route_topk", "moe_layer_workspace_bytes", "moe_expert_ffn_q", "moe_layer_decode",
                           "dense_gemv_q", "moe_last_error", "moe_version", "moe_workspace_status",
                           "moe_layer_decode_noalloc", "moe_rmsnorm", "moe_router_topk_scores",
-                          "moe_block_workspace_bytes", "moe_block_decode"}
+                          "moe_block_workspace_bytes", "moe_block_decode", "moe_quantize_mx_e4m3"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.moe_version() >= 100
@@ -188,3 +188,14 @@ def test_block_steps_validation(lib):
     assert lib.moe_block_decode(ctypes.byref(B), FAKE, 4, FAKE, None, None, 0, FAKE2, need - 1,
                                 None) == moeq.MOE_EWORKSPACE
     assert lib.moe_block_decode(ctypes.byref(B), None, 4, FAKE, None, None, 0, FAKE2, need, None) == moeq.MOE_EINVAL
+
+
+def test_quantiser_validation(lib):
+    """The MX e4m3 activation quantiser refuses bad shapes and NULL buffers
+    before anything is enqueued."""
+    assert lib.moe_quantize_mx_e4m3(FAKE, 2, 48, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert "H=48" in _err(lib)
+    assert lib.moe_quantize_mx_e4m3(FAKE, 0, 64, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert lib.moe_quantize_mx_e4m3(None, 2, 64, FAKE, FAKE, None) == moeq.MOE_EINVAL
+    assert lib.moe_quantize_mx_e4m3(FAKE, 2, 64, FAKE, None, None) == moeq.MOE_EINVAL
+    assert "scales" in _err(lib)
