@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 DEFAULT_CONFIG = "batched_decode"
 COPY_BYTES = 512 << 20           # calibration copy: reads and writes this many bytes
@@ -58,6 +59,10 @@ def kernel_of(workload, batch=1):
             "wide_block": "block_step", "batched_block": "block_step"}.get(workload, "kernel")
 
 
+ARITH = {"bf16": "low-bit weights decoded exactly, bf16 activations, fp32 accumulate, bf16 output",
+         "mxfp8": "activations quantised to MX e4m3 + UE8M0/32; MX weights on the scaled fp8 x fp6/fp4 matrix "
+                  "cores (many-token path), otherwise decoded exactly against the dequantised activations; "
+                  "fp32 accumulate, bf16 output"}
 FMT_NAMES = {1: "e2m1+e4m3/16", 2: "e2m3+ue8m0/128", 3: "e2m1+ue8m0/32", 4: "int4+fp16/64", 5: "e2m3+e4m3/16"}
 
 
@@ -70,6 +75,8 @@ def parse():
     p.add_argument("--batch", type=int, default=1, help="GEMV tokens (dense_gemv_e2m3 only)")
     p.add_argument("--fmt", type=int, default=0,
                    help="weight format of the workload (1..5; 0: the workload's own): measures the format variants")
+    p.add_argument("--act", choices=("bf16", "mxfp8"), default="bf16",
+                   help="activations entering gate|up: bf16, or MX e4m3 + UE8M0/32 (MOE_ACT_MXFP8)")
     p.add_argument("--replicas", type=int, default=0, help="weight replicas (0: enough for >= 4x the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -400,6 +407,8 @@ def main():
     errs = None
 
     if isinstance(cfg, configs.GemvConfig):
+        if a.act != "bf16":
+            sys.exit("--act mxfp8 applies to the layer workloads")
         B = a.batch
         c, s = synth.gemv_weights(cfg)
         wbytes = c.nbytes + s.nbytes
@@ -466,6 +475,9 @@ def main():
                              shared_inter=cfg.shared_inter, shared=shared_copies[i % n_sh] if n_sh else None)
                   for i in range(n)]
         is_block = cfg.name.endswith("_block")
+        act_flag = moeq.MOE_ACT_MXFP8 if a.act == "mxfp8" else 0
+        if act_flag and is_block:
+            sys.exit("--act mxfp8 applies to the layer workloads")
         xh = synth.hidden_states(cfg)
         x = dev_bf16(xh)
         out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
@@ -477,7 +489,8 @@ def main():
             xs_host = [synth.hidden_states(cfg, sub=i) for i in range(NL)]
             xs = [dev_bf16(v) for v in xs_host]
             ws = moeq.block_workspace(blocks[0], T)
-            calls = [(lambda i=i: moeq.moe_block_decode(blocks[i], xs[i % NL], out=out, ws=ws)) for i in range(n)]
+            calls = [(lambda i=i: moeq.moe_block_decode(blocks[i], xs[i % NL], out=out, flags=act_flag, ws=ws))
+                     for i in range(n)]
             logits_host = []
             for v in xs_host:
                 xn = oracle_bf16_rmsnorm(v, synth.norm_gamma(cfg), cfg.norm_eps)
@@ -486,7 +499,7 @@ def main():
             logits_host = [synth.router_logits(cfg, sub=i) for i in range(NL)]
             logits = [torch.from_numpy(l).cuda() for l in logits_host]
             ws = moeq.workspace(layers[0], T)
-            calls = [(lambda i=i: moeq.moe_layer_decode(layers[i], x, logits[i % NL], out=out, ws=ws))
+            calls = [(lambda i=i: moeq.moe_layer_decode(layers[i], x, logits[i % NL], out=out, flags=act_flag, ws=ws))
                      for i in range(n)]
         if a.profile_steps:
             for i in range(a.warmup + a.profile_steps):
@@ -522,6 +535,8 @@ def main():
             workload["pairs"] = pairs
             workload["mfma_tflops_algorithmic"] = flops / per / 1e12
             workload["mfma_frac_of_bf16_dense_peak"] = flops / per / 1e12 / MFMA_BF16_PEAK_TFLOPS
+            if act_flag:
+                workload["mfma_frac_of_fp8_dense_peak"] = flops / per / 1e12 / MFMA_FP8_PEAK_TFLOPS
         # error figures of the last timed call's bf16 output against the oracle
         # (all tokens; the first 16 of a many-token call)
         last = (a.warmup + a.steps - 1) % n
@@ -537,7 +552,10 @@ def main():
                                            xs_host[last % NL][:nt], synth.norm_gamma(cfg), synth.router_weights(cfg),
                                            cfg.norm_eps, shared=sh, shared_inter=cfg.shared_inter)
         else:
-            _, _, ref = oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xh[:nt], lg,
+            xr = xh[:nt]
+            if act_flag:    # the reference layer on the oracle's quantised-then-dequantised activations
+                xr = oracle.bf16_round(oracle.dequantize_mx_e4m3(*oracle.quantize_mx_e4m3(xr)))
+            _, _, ref = oracle.layer(cfg.fmt, cfg.hidden, cfg.inter, cfg.experts, cfg.top_k, ex, xr, lg,
                                      shared=sh, shared_inter=cfg.shared_inter)
         errs = err_figures(outb[:nt], ref)
         errs["sample"] = "%d token(s) of the last timed call" % nt
@@ -568,10 +586,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if a.act == "bf16" else "e4m3 activations",
         "data": "synthetic (seeded generator; random-init weights of the workload's shapes)",
-        "config": dict(workload, launch="hipgraph", arithmetic="low-bit weights decoded exactly, bf16 activations, "
-                       "fp32 accumulate, bf16 output", graph_replays_per_window=tm["graph_replays_per_window"],
+        "config": dict(workload, launch="hipgraph", arithmetic=ARITH[a.act], graph_replays_per_window=tm["graph_replays_per_window"],
                        eager_repeats_per_window=tm["eager_repeats_per_window"], windows=tm["windows"],
                        window_min_ms=WINDOW_S * 1e3, statistic="median of windows"),
         "effective_weight_GBps": achieved,

@@ -616,6 +616,209 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
     }
 }
 
+// An empty asm that "rewrites" a unit's registers: placed after the step's
+// vmcnt wait, it keeps the compiler from hoisting their uses above that wait
+// (its own waitcnt pass would then also wait for younger loads).
+template <int FMT>
+__device__ inline void pf_pin_unit(Unit<FMT> &U) {
+    if constexpr (!Fmt<FMT>::SIX)
+        asm volatile("" : "+v"(U.c.x), "+v"(U.c.y), "+v"(U.c.z), "+v"(U.c.w), "+v"(U.s));
+    else
+        asm volatile("" : "+v"(U.c0.x), "+v"(U.c0.y), "+v"(U.c1.x), "+v"(U.c1.y), "+v"(U.c2.x), "+v"(U.c2.y),
+                     "+v"(U.s));
+}
+
+// Down projection with the block's h resident in LDS.  y = Wd (h_hi + h_lo)
+// has a short K (the intermediate width, 512 here), so a workgroup per (block,
+// tile of rows) would spend most of its life filling its pipeline.  Instead
+// one workgroup of eight waves takes a whole block: it copies the block's
+// h_hi and h_lo rows into LDS once (64 rows x 1 KiB per plane), and every wave
+// then streams its weight rows for all H outputs, 32 rows (two 16-row groups)
+// per pass, with PD K steps of weight units in flight in registers and no
+// barrier after the copy -- the weights are private to the wave.  Row r of a
+// plane is 1 KiB; its 16-byte chunk c sits at c ^ (r & 15), so the 16 rows a
+// quarter-wave reads fall on distinct banks.
+//
+// Each pass ends with its y stores.  On this part vmcnt counts stores as well
+// as loads, and a store may complete before older loads, so the only safe
+// wait for a load group is "at most (younger loads) outstanding", which also
+// waits for every store issued since.  The pass's last step therefore waits
+// for the next step's group before it issues the stores, that next step
+// skips its wait, and the stores have its whole compute time to complete
+// before the step after it waits again.
+constexpr int PF_DR_KMAX = 512;
+constexpr int PF_DR_RG = 2;                 // 16-row groups per wave per pass
+constexpr int PF_DR_PLANE = PF_MB * PF_DR_KMAX * 2;
+// K steps in flight: 4 when a pass has 4 K steps (K = 512), else 2 (K = 256, 384)
+
+template <int FMT, int NSUB, int PD>
+__device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const float *s_scale, int M, int p0, int K,
+                                        const uint8_t *wc, const uint8_t *ws) {
+    constexpr int NWAVES = 8, RG = PF_DR_RG, R = PD + 1;
+    constexpr int PER_GROUP = RG * PfUnitLoads<FMT>::n;
+    constexpr int T0 = (PD - 1) * PER_GROUP;            // loads younger than a step's group
+    constexpr bool WLO = pf_split_w<FMT>();
+    constexpr int CP = 2 * 16 * NSUB / NWAVES;          // 1 KiB row copies per wave (both planes)
+    static_assert((2 * 16 * NSUB) % NWAVES == 0, "copies per wave");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int H = a.L.H;
+    const int nK = K / PF_KS;                           // K steps per pass (>= PD)
+    constexpr int ROWS = NWAVES * RG * 16;              // rows per pass
+    const int npass = (H + ROWS - 1) / ROWS;
+    const int nstep = npass * nK;
+    using F = Fmt<FMT>;
+    const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
+
+    // the block's h rows into LDS: copy q of this wave is row (q * 8 + wv) of
+    // the two planes; lane = the row's 16-byte position, holding chunk lane ^ (row & 15)
+    {
+        const uint64_t bytes = (uint64_t)a.off[a.NS] * a.Imax * 2;
+        const __amdgpu_buffer_rsrc_t src[2] = {rsrc_of(a.h_hi, bytes), rsrc_of(a.h_lo, bytes)};
+#pragma unroll
+        for (int q = 0; q < CP; ++q) {
+            const int g = q * NWAVES + wv;              // 0 .. 32 NSUB - 1
+            constexpr int HALF = CP / 2;                // copies q < HALF are h_hi rows (g < 16 NSUB)
+            const int pl = q < HALF ? 0 : 1, row = g - pl * 16 * NSUB;
+            const int c = lane ^ (row & 15);
+            const u32 voff = c * 8 < K ? ((u32)(p0 + min(row, M - 1)) * (u32)a.Imax + (u32)c * 8u) * 2u : 0x7FFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src[pl], (lds_void_t *)(s_h + pl * PF_DR_PLANE + row * 1024), 16,
+                                                     voff, 0, 0, 0);
+        }
+    }
+    asm volatile("" ::: "memory");     // the copies are issued before the weight loads below
+
+    // weight units of flattened step f = pass * nK + j: unit 4 j + lg of rows
+    // pass * ROWS + wv * 32 + 16 g + lr (clamped into the matrix; results dropped)
+    Unit<FMT> wq[R][RG];
+    auto load_w = [&](Unit<FMT> (&U)[RG], int f) {
+        const int ff = min(f, nstep - 1);
+        const int ps = ff / nK, j = ff - ps * nK;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int n = min(ps * ROWS + wv * 16 * RG + 16 * g + lr, H - 1);
+            load_unit<FMT>(U[g], wc + (size_t)n * crb, ws + (size_t)n * srb, 4 * j + lg);
+        }
+    };
+    f32x4_t acc[RG][NSUB];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    [&]<int... I>(std::integer_sequence<int, I...>) { (load_w(wq[I], I), ...); }(std::make_integer_sequence<int, PD>{});
+    pf_wait_vm<PD * PER_GROUP>();                       // this wave's h copies have landed
+    pf_barrier();                                       // ... and every wave's (weights stay in flight)
+
+    auto step = [&](auto dc, int f) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + PD) % R;
+        const int ps = f / nK, j = f - ps * nK;
+        // step f's units have landed (the first step of a pass: waited for
+        // before the previous pass's stores)
+        if (!(ps > 0 && j == 0)) pf_wait_vm<T0>();
+#pragma unroll
+        for (int g = 0; g < RG; ++g) pf_pin_unit<FMT>(wq[d][g]);
+        bf16x8_t bw[RG][4], bwl[RG][4];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) pf_unit_to_b<FMT>(wq[d][g], s_scale, bw[g], bwl[g]);
+        load_w(wq[dn], f + PD);
+        asm volatile("" ::: "memory");                  // the stores below stay after these loads
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 16 * j + 4 * lg + s;          // chunk: K 8c .. 8c+7
+            bf16x8_t ah[NSUB], al[NSUB];
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+                const int row = 16 * m + lr;
+                const uint8_t *ap = s_h + row * 1024 + ((c ^ (row & 15)) << 4);
+                ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
+                al[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PF_DR_PLANE));
+            }
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m)
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bw[g][s], acc[g][m], 0, 0, 0);
+                    acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bw[g][s], acc[g][m], 0, 0, 0);
+                    if (WLO) {
+                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bwl[g][s], acc[g][m], 0, 0, 0);
+                        acc[g][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bwl[g][s], acc[g][m], 0, 0, 0);
+                    }
+                }
+        }
+        if (j == nK - 1) {
+            pf_wait_vm<T0>();                           // step f + 1's units, before any store
+            // the pass's stores: lane holds tokens 16m + 4 lg + i of row n
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                const int n = ps * ROWS + wv * 16 * RG + 16 * g + lr;
+#pragma unroll
+                for (int m = 0; m < NSUB; ++m) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * m + 4 * lg + i;
+                        if (n < H && t < M) a.y[(size_t)(p0 + t) * H + n] = acc[g][m][i];
+                    }
+                    acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    };
+    int f = 0;
+    for (; f + R <= nstep; f += R)
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (step(std::integral_constant<int, I>{}, f + I), ...);
+        }(std::make_integer_sequence<int, R>{});
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((f + I < nstep ? step(std::integral_constant<int, I>{}, f + I) : void()), ...);
+    }(std::make_integer_sequence<int, R - 1>{});
+    pf_wait_vm<0>();    // the loads issued past the end land before the wave exits
+}
+
+// One workgroup (eight waves) per block of up to 64 tokens.
+template <int FMT>
+__global__ __launch_bounds__(512, 1) void pf_down_res_kernel(PfArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_h[2 * PF_DR_PLANE];
+    __shared__ float s_scale[LUT_SCALE];
+    const int b = blockIdx.x;
+    if (b >= a.nblk[0]) return;
+    const int packed = a.blk[b];
+    const int slot = packed >> 16, m0 = packed & 0xFFFF;
+    const int E = a.L.E, H = a.L.H;
+    const bool shared = slot == E;
+    const int K = shared ? a.L.Ish : a.L.I;
+    const int M = min(PF_MB, a.cnt[slot] - m0);
+    const int nsub = (M + 15) >> 4;
+    const int p0 = a.off[slot] + m0;
+    if (Fmt<FMT>::SCALE == SC_E4M3) {   // the other scales are converted arithmetically
+        Luts Lt;
+        Lt.pair = nullptr;
+        Lt.scale = s_scale;
+        build_luts<FMT>(Lt, threadIdx.x, 512, false);
+        __syncthreads();
+    }
+    using F = Fmt<FMT>;
+    const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
+    const uint8_t *wc = shared ? a.L.sh2c : a.L.w2c + (size_t)slot * H * crb;
+    const uint8_t *ws = shared ? a.L.sh2s : a.L.w2s + (size_t)slot * H * srb;
+    if (K / PF_KS >= 4) {
+        switch (nsub) {
+            case 1: pf_down_res_main<FMT, 1, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            case 2: pf_down_res_main<FMT, 2, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            case 3: pf_down_res_main<FMT, 3, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            default: pf_down_res_main<FMT, 4, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+        }
+    } else {
+        switch (nsub) {
+            case 1: pf_down_res_main<FMT, 1, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            case 2: pf_down_res_main<FMT, 2, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            case 3: pf_down_res_main<FMT, 3, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+            default: pf_down_res_main<FMT, 4, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+        }
+    }
+}
+
 // Gate | up on the scaled matrix cores for the MX weight formats (e2m1 or
 // e2m3 codes with UE8M0 scales per 32, or per 128 = four blocks of 32 with one
 // byte) and MX e4m3 activations (scale per 32): v_mfma_scale_f32_16x16x128_f8f6f4
@@ -625,31 +828,216 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
 // group g holds K 16g .. 16g+15 in its first 16 bytes and 64+16g .. 64+16g+15
 // in its last 16; the scale of K block b (K 32b .. 32b+31) is lane group b's
 // scale byte, for A and for B alike, whichever lanes hold that block's data.
-// So for the 128-wide K step s, B lane group h loads weight unit 4s + h with
-// its scale, and A lane group g loads its two 16-byte pieces of the token's
-// codes and the scale of activation block 4s + g: one instruction per step.
-// One workgroup per (block of 64 tokens, tile of 64 intermediate rows), four
-// waves of 16 gate and the same 16 up rows; the next K step's loads are issued
-// before this step's MFMAs.  The epilogue is the bf16 path's: h = silu(g) * u
-// as a bf16 hi + lo pair.
+//
+// A K step is 256 wide (eight 32-weight units), two instructions.  Each lane
+// loads two consecutive units of its row, 8s + 2h and 8s + 2h + 1 (so the four
+// lane groups read 128 contiguous bytes of the row for e2m1), and instruction
+// t of the step takes unit 8s + 2h + t in lane group h.  A dot product does
+// not care in which order its terms are summed, so the instruction's K block b
+// simply is unit 8s + 2b + t: lane group g then takes, from the staged codes,
+// the half g%2 of units 8s + 2(g/2) + t and 8s + 4 + 2(g/2) + t, and the scale
+// of activation block 8s + 2g + t.
+//
+// The pipeline is the bf16 path's (pf_gemm_main) with two steps in flight:
+// the 64 x 256 byte code tile of a K step is copied into an LDS stage by
+// buffer-load-to-LDS, two steps ahead, together with each lane's weight units and its two activation scale
+// bytes per 16-token sub-tile, so one vmcnt wait per step covers all of them.
+// Stage rows are 256 bytes; the 16-byte piece c of row r sits at c ^ (r & 15),
+// so the 16 rows a quarter-wave reads fall on distinct banks.  H must be a
+// multiple of 256 (every unit of every step is then inside the row).
 typedef __attribute__((ext_vector_type(8))) int v8i_t;
 
-template <int FMT>
-__device__ inline v8i_t pf_mx_b(const Unit<FMT> &U) {
-    v8i_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (!Fmt<FMT>::SIX) {
-        v[0] = (int)U.c.x; v[1] = (int)U.c.y; v[2] = (int)U.c.z; v[3] = (int)U.c.w;
-    } else {
-        v[0] = (int)U.c0.x; v[1] = (int)U.c0.y; v[2] = (int)U.c1.x; v[3] = (int)U.c1.y; v[4] = (int)U.c2.x;
-        v[5] = (int)U.c2.y;
-    }
-    return v;
-}
+constexpr int PF_MX_KS = 256;                         // K per step = bytes per staged e4m3 row
+constexpr int PF_MX_PD = 2;                           // K steps in flight
+
+// Two consecutive weight units of a row (codes) and their scale byte(s).
+template <int FMT> struct MxPair {
+    static constexpr int ND = Fmt<FMT>::SIX ? 12 : 8;
+    u32 c[ND];
+    u32 s;
+};
 
 template <int FMT>
-__global__ __launch_bounds__(256) void pf_gateup_mx_kernel(PfArgs a, int NT) {
-    static_assert(Fmt<FMT>::SCALE == SC_UE8M0, "MX weight formats only");
+__device__ inline void mx_load_pair(MxPair<FMT> &P, const uint8_t *codes, const uint8_t *scales, int u0) {
+    const uint8_t *p = codes + (int64_t)u0 * Fmt<FMT>::UNIT_CODE_BYTES;
+#pragma unroll
+    for (int q = 0; q < MxPair<FMT>::ND / 4; ++q) {
+        const uint4 v = ldg16(p + 16 * q);
+        P.c[4 * q] = v.x; P.c[4 * q + 1] = v.y; P.c[4 * q + 2] = v.z; P.c[4 * q + 3] = v.w;
+    }
+    if constexpr (Fmt<FMT>::BLOCK == 32) P.s = *reinterpret_cast<const uint16_t *>(scales + u0);   // u0 even
+    else P.s = scales[u0 / (Fmt<FMT>::BLOCK / 32)];                 // both units in one block
+}
+
+// B operand and scale byte of unit t (0, 1) of the pair
+template <int FMT>
+__device__ inline v8i_t mx_b(const MxPair<FMT> &P, int t) {
+    v8i_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    constexpr int W = Fmt<FMT>::SIX ? 6 : 4;
+#pragma unroll
+    for (int i = 0; i < W; ++i) v[i] = (int)P.c[W * t + i];
+    return v;
+}
+template <int FMT>
+__device__ inline int mx_bs(const MxPair<FMT> &P, int t) {
+    return Fmt<FMT>::BLOCK == 32 ? (int)((P.s >> (8 * t)) & 0xFF) : (int)(P.s & 0xFF);
+}
+
+// An empty asm that "rewrites" the registers: placed after the step's vmcnt
+// wait, it keeps the compiler from hoisting their uses above that wait (its
+// own waitcnt pass would then also wait for younger loads).
+template <int FMT>
+__device__ inline void mx_pin(MxPair<FMT> &P) {
+#pragma unroll
+    for (int i = 0; i < MxPair<FMT>::ND; ++i) asm volatile("" : "+v"(P.c[i]));
+    asm volatile("" : "+v"(P.s));
+}
+
+template <int FMT, int NSUB>
+__device__ inline void pf_mx_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2,
+                                  const int *s_tok, int M, int p0, int Is, int n0, const uint8_t *const (&rc)[2],
+                                  const uint8_t *const (&rs)[2]) {
+    constexpr int NWAVES = 4, NB = 2;
     constexpr int BFMT = Fmt<FMT>::SIX ? 2 : 4;        // fp6 e2m3 or fp4 e2m1 operand
+    constexpr int PD = PF_MX_PD;
+    constexpr int R = PD + 1;
+    static_assert(R == 3, "three stage objects");
+    constexpr int NDMA = NSUB * 16 * PF_MX_KS / 1024;  // 1 KiB copies per stage (4 per sub-tile)
+    constexpr int DPW = NDMA / NWAVES;                 // = NSUB
+    constexpr int PER_GROUP = DPW + NB * (MxPair<FMT>::ND / 4 + 1) + NSUB;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int H = a.L.H, HB = H / 32;
+    const int nK = H / PF_MX_KS;
+
+    const __amdgpu_buffer_rsrc_t src = rsrc_of(a.xq, (uint64_t)a.T * H);
+    u32 row_off[DPW], col_k[DPW];
+    int dst_off[DPW];
+#pragma unroll
+    for (int q = 0; q < DPW; ++q) {
+        const int g = q * NWAVES + wv;                 // copy index in the stage
+        const int P = g * 64 + lane;                   // 16-byte position in the stage
+        const int row = P >> 4;
+        const int logical = (P & 15) ^ (row & 15);
+        row_off[q] = (u32)s_tok[min(row, M - 1)] * (u32)H;
+        col_k[q] = (u32)logical * 16u;
+        dst_off[q] = g * 1024;
+    }
+    // this lane's activation scale rows (one per sub-tile)
+    const uint8_t *srow[NSUB];
+#pragma unroll
+    for (int m = 0; m < NSUB; ++m) srow[m] = a.xs + (size_t)s_tok[min(16 * m + lr, M - 1)] * HB;
+
+    auto stage = [&](auto sc) -> uint8_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0) return st0;
+        else if constexpr (S == 1) return st1;
+        else return st2;
+    };
+    MxPair<FMT> wq[R][NB];
+    u32 sq[R][NSUB];
+    // the loads of K step j (clamped to the last step past the end: no branch,
+    // results unused): activation codes into stage sc, weight units and scale
+    // bytes into register slot sc
+    auto issue = [&](auto sc, int j) {
+        constexpr int S = decltype(sc)::value;
+        uint8_t *st = stage(sc);
+        const int jj = min(j, nK - 1);
+        const u32 kb = (u32)jj * PF_MX_KS;
+#pragma unroll
+        for (int q = 0; q < DPW; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t *)(st + dst_off[q]), 16, row_off[q] + kb + col_k[q],
+                                                     0, 0, 0);
+        const int u0 = jj * 8 + 2 * lg;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mx_load_pair<FMT>(wq[S][b], rc[b], rs[b], u0);
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) sq[S][m] = *reinterpret_cast<const uint16_t *>(srow[m] + u0);
+    };
+
+    f32x4_t acc[NB][NSUB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) acc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+
+    auto step = [&](auto dc, int it) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + PD) % R;
+        pf_wait_vm<(PD - 1) * PER_GROUP>();          // this wave's step-it loads have landed
+        pf_barrier();                                   // ... and every wave's; stage (it-1) % R is free
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mx_pin<FMT>(wq[d][b]);
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) asm volatile("" : "+v"(sq[d][m]));
+        issue(std::integral_constant<int, dn>{}, it + PD);
+        const MxPair<FMT> (&w)[NB] = wq[d];
+        const u32 (&sa)[NSUB] = sq[d];
+        const uint8_t *st = stage(dc);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // pieces 4(g/2) + 2t + g%2 and 8 + the same, of rows 16m + lr
+            const int q0 = 4 * (lg >> 1) + 2 * t + (lg & 1);
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+                const int row = 16 * m + lr;
+                const u32x4_t p0v = *reinterpret_cast<const u32x4_t *>(st + row * PF_MX_KS + ((q0 ^ (row & 15)) << 4));
+                const u32x4_t p1v =
+                    *reinterpret_cast<const u32x4_t *>(st + row * PF_MX_KS + (((8 + q0) ^ (row & 15)) << 4));
+                const v8i_t av = {(int)p0v[0], (int)p0v[1], (int)p0v[2], (int)p0v[3],
+                                  (int)p1v[0], (int)p1v[1], (int)p1v[2], (int)p1v[3]};
+                const int sam = (int)((sa[m] >> (8 * t)) & 0xFF);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[b][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, mx_b<FMT>(w[b], t), acc[b][m], 0,
+                                                                                 BFMT, 0, sam, 0, mx_bs<FMT>(w[b], t));
+            }
+        }
+    };
+    int it = 0;
+    for (; it + R <= nK; it += R) {
+        step(I0{}, it);
+        step(I1{}, it + 1);
+        step(I2{}, it + 2);
+    }
+    if (it < nK) step(I0{}, it);
+    if (it + 1 < nK) step(I1{}, it + 1);
+    pf_wait_vm<0>();    // the copies issued past the end land before the workgroup's LDS is reused
+
+    // epilogue: lane holds tokens 16m + 4 lg + i, weight row n0 + 16 wv + lr
+    const int nn = n0 + wv * 16 + lr;
+    if (nn >= Is) return;
+#pragma unroll
+    for (int m = 0; m < NSUB; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * m + 4 * lg + i;
+            if (t >= M) continue;
+            const size_t p = (size_t)(p0 + t);
+            const float h = silu_f32(acc[0][m][i]) * acc[1][m][i];
+            const uint16_t hi = f32_to_bf16_rne(h);
+            const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
+            a.h_hi[p * a.Imax + nn] = hi;
+            a.h_lo[p * a.Imax + nn] = lo;
+        }
+    }
+}
+
+// One workgroup per (block of up to 64 tokens, tile of 64 intermediate rows):
+// four waves, each with 16 rows of gate and the same 16 rows of up.
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void pf_gateup_mx_kernel(PfArgs a, int NT) {
+    static_assert(Fmt<FMT>::SCALE == SC_UE8M0, "MX weight formats only");
+    constexpr int STAGE_BYTES = 4 * 16 * PF_MX_KS;
+    __shared__ __attribute__((aligned(1024))) uint8_t mx_st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t mx_st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t mx_st2[STAGE_BYTES];
     __shared__ int s_tok[PF_MB];
     const int wid = blockIdx.x;
     const int win = wid / (8 * NT), q = wid - win * 8 * NT;
@@ -663,96 +1051,25 @@ __global__ __launch_bounds__(256) void pf_gateup_mx_kernel(PfArgs a, int NT) {
     const int n0 = nt * 64;
     if (n0 >= Is) return;
     const int M = min(PF_MB, a.cnt[slot] - m0);
+    const int nsub = (M + 15) >> 4;
     const int p0 = a.off[slot] + m0;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int lr = lane & 15;
     if (tid < PF_MB) s_tok[tid] = a.tok[(size_t)slot * a.T + m0 + min(tid, M - 1)];
-    __syncthreads();
 
     using F = Fmt<FMT>;
     const int64_t crb = F::code_row_bytes(H), srb = F::scale_row_bytes(H);
     const uint8_t *wc = shared ? a.L.sh13c : a.L.w13c + (size_t)slot * 2 * Is * crb;
     const uint8_t *ws = shared ? a.L.sh13s : a.L.w13s + (size_t)slot * 2 * Is * srb;
     const int n = min(n0 + wv * 16 + lr, Is - 1);     // rows past Is: a valid row, result dropped
-    const uint8_t *rc[2] = {wc + (size_t)n * crb, wc + (size_t)(Is + n) * crb};
-    const uint8_t *rs[2] = {ws + (size_t)n * srb, ws + (size_t)(Is + n) * srb};
-    const int UK = H / 32, nK = (H + 127) / 128, HB = H / 32;
-    const uint8_t *arow[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) arow[m] = a.xq + (size_t)s_tok[min(16 * m + lr, M - 1)] * H;
-    const uint8_t *srow[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) srow[m] = a.xs + (size_t)s_tok[min(16 * m + lr, M - 1)] * HB;
-    const int nsub = (M + 15) >> 4;
-
-    Unit<FMT> wu[2][2];
-    uint4 ax[2][4][2];
-    u32 as[2][4];
-    auto load = [&](int st, int j) {
-        const int u = min(j * 4 + lg, UK - 1);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) load_unit<FMT>(wu[st][g], rc[g], rs[g], u);
-        // the two activation pieces, K 128 j + 16 lg and 128 j + 64 + 16 lg (kept inside the row)
-        const int k0 = min(128 * j + 16 * lg, H - 16), k1 = min(128 * j + 64 + 16 * lg, H - 16);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            ax[st][m][0] = *reinterpret_cast<const uint4 *>(arow[m] + k0);
-            ax[st][m][1] = *reinterpret_cast<const uint4 *>(arow[m] + k1);
-            as[st][m] = srow[m][u];
-        }
-    };
-    f32x4_t acc[2][4];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[g][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto step = [&](int st, int j) {
-        // K blocks past the row's end: weights 0 with unit scales, so they add exactly 0
-        const bool live = j * 4 + lg < UK;
-        v8i_t bw[2];
-        int bs[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            bw[g] = live ? pf_mx_b<FMT>(wu[st][g]) : v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
-            bs[g] = live ? (int)(wu[st][g].s & 0xFF) : 127;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m < nsub) {
-                const v8i_t av = {(int)ax[st][m][0].x, (int)ax[st][m][0].y, (int)ax[st][m][0].z, (int)ax[st][m][0].w,
-                                  (int)ax[st][m][1].x, (int)ax[st][m][1].y, (int)ax[st][m][1].z, (int)ax[st][m][1].w};
-                const int sa = live ? (int)as[st][m] : 127;
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    acc[g][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[g], acc[g][m], 0, BFMT, 0, sa, 0,
-                                                                                 bs[g]);
-            }
-        }
-    };
-    load(0, 0);
-    for (int j = 0; j < nK; j += 2) {
-        load(1, j + 1);
-        step(0, j);
-        if (j + 1 >= nK) break;
-        load(0, j + 2);
-        step(1, j + 1);
-    }
-    // epilogue: lane holds tokens 16m + 4 lg + i, weight row n0 + 16 wv + lr
-    const int nn = n0 + wv * 16 + lr;
-    if (nn >= Is) return;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * m + 4 * lg + i;
-            if (t >= M) continue;
-            const size_t p = (size_t)(p0 + t);
-            const float h = silu_f32(acc[0][m][i]) * acc[1][m][i];
-            const uint16_t hi = f32_to_bf16_rne(h);
-            const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
-            a.h_hi[p * a.Imax + nn] = hi;
-            a.h_lo[p * a.Imax + nn] = lo;
-        }
+    const uint8_t *const rc[2] = {wc + (size_t)n * crb, wc + (size_t)(Is + n) * crb};
+    const uint8_t *const rs[2] = {ws + (size_t)n * srb, ws + (size_t)(Is + n) * srb};
+    __syncthreads();   // s_tok
+    switch (nsub) {
+        case 1: pf_mx_main<FMT, 1>(a, mx_st0, mx_st1, mx_st2, s_tok, M, p0, Is, n0, rc, rs); break;
+        case 2: pf_mx_main<FMT, 2>(a, mx_st0, mx_st1, mx_st2, s_tok, M, p0, Is, n0, rc, rs); break;
+        case 3: pf_mx_main<FMT, 3>(a, mx_st0, mx_st1, mx_st2, s_tok, M, p0, Is, n0, rc, rs); break;
+        default: pf_mx_main<FMT, 4>(a, mx_st0, mx_st1, mx_st2, s_tok, M, p0, Is, n0, rc, rs); break;
     }
 }
 

@@ -71,7 +71,11 @@ static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     } else {
         hipLaunchKernelGGL((pf_gemm_kernel<FMT, false>), dim3(l.nblk_max * nt_gu), dim3(256), 0, s, p, nt_gu);
     }
-    hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
+    // down: the h-resident kernel when every expert's K fits its LDS tile
+    const bool res = p.L.I % PF_KS == 0 && p.L.I >= 2 * PF_KS && p.L.I <= PF_DR_KMAX &&
+                     (p.L.Ish == 0 || (p.L.Ish % PF_KS == 0 && p.L.Ish >= 2 * PF_KS && p.L.Ish <= PF_DR_KMAX));
+    if (res) hipLaunchKernelGGL((pf_down_res_kernel<FMT>), dim3(l.nblk_max), dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
     hipLaunchKernelGGL(pf_combine_kernel, dim3(p.T), dim3(PF_THREADS), 0, s, p);
     return hipGetLastError();
 }
@@ -112,8 +116,8 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
         p.xs = nullptr;
         if (a.act_mx) {
             // the chunk's activations to MX e4m3; MX weights take the codes on the
-            // scaled matrix cores, the other formats the dequantised bf16 rows
-            const bool mx = L.fmt == FMT_E2M3 || L.fmt == FMT_MXFP4;
+            // scaled matrix cores (H a multiple of 256), the rest the dequantised bf16 rows
+            const bool mx = (L.fmt == FMT_E2M3 || L.fmt == FMT_MXFP4) && L.H % PF_MX_KS == 0;
             uint16_t *xd = (uint16_t *)(ws + l.xd);
             hipError_t e = launch_mx_quant(p.x, Tc, L.H, ws + l.xq, ws + l.xs, mx ? nullptr : xd, s);
             if (e != hipSuccess) return e;

@@ -2,7 +2,8 @@
 against the oracle: several tiles with ragged tails in H, I and the shared
 expert's width, both formats, experts with no tokens and with more tokens
 than one block holds, fixed-expert calls, chunking past 2,048 tokens, and the
-full-size 2,048-token workload on sampled tokens."""
+full-size 2,048-token workload on sampled tokens; the down projection with
+the block's h resident in LDS for every weight format."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +28,11 @@ PF_E2M3 = MoEConfig("pf_e2m3", tokens=90, hidden=384, experts=12, top_k=3, inter
 # more than one chunk of 2,048 tokens
 PF_CHUNKED = MoEConfig("pf_chunked", tokens=2085, hidden=256, experts=8, top_k=2, inter=128, shared_inter=64)
 CFGS = [PF_SMALL, PF_SHARED, PF_E2M3]
+# down with the block's h resident in LDS: I = 512 (four K steps a pass, routed
+# experts) and Ish = 384 (three), H = 768 (three passes of 256 rows), experts
+# with two blocks (up to 64 tokens and a ragged rest), every weight format
+PF_RES = [MoEConfig("pf_res_f%d" % f, tokens=150, hidden=768, experts=6, top_k=2, inter=512, shared_inter=384,
+                    fmt=f) for f in (1, 2, 3, 4, 5)]
 _layers = {}
 
 
@@ -62,6 +68,14 @@ def _check(cfg, x, l, idx, w, out32, out16):
 def test_prefill_parity(cfg):
     require_gpu()
     print("prefill parity", cfg.name, flush=True)
+    x, l = synth.hidden_states(cfg), synth.router_logits(cfg)
+    _check(cfg, x, l, *_run(cfg, x, l))
+
+
+@pytest.mark.parametrize("cfg", PF_RES, ids=lambda c: c.name)
+def test_prefill_resident_down(cfg):
+    require_gpu()
+    print("prefill resident down", cfg.name, flush=True)
     x, l = synth.hidden_states(cfg), synth.router_logits(cfg)
     _check(cfg, x, l, *_run(cfg, x, l))
 
