@@ -137,13 +137,19 @@ def traffic_summary(a):
             raise SystemExit("no kernel matching %r in the counter file" % key)
         vals = [v for n in names for v in d[n]]
         return names, vals
-    if want == "layer_step":
-        # the many-token step is five launches: sum them, per step
+    if want in ("layer_step", "block_step"):
+        # a step of several launches (the many-token layer: route, group, gate|up,
+        # down, combine; the block: norm, router scores, layer): sum them, per step
+        if want == "layer_step":
+            keys, first = ("pf_", "route_kernel", "mx_quant_kernel"), "pf_group"
+        else:
+            keys, first = ("rmsnorm_kernel", "router_kernel", "decode1_kernel", "decodeT_kernel"), "rmsnorm_kernel"
+
         def step(d):
-            names = [n for n in d if "pf_" in n or "route_kernel" in n]
-            steps = sum(len(d[n]) for n in names if "pf_group" in n)
+            names = [n for n in d if any(k in n for k in keys)]
+            steps = sum(len(d[n]) for n in names if first in n)
             if not steps:
-                raise SystemExit("no many-token step in the counter file")
+                raise SystemExit("no %s in the counter file" % want)
             return names, [sum(v for n in names for v in d[n]) / steps] * steps
         kn, kf = step(fetch)
         _, kw = step(write)
@@ -163,7 +169,7 @@ def traffic_summary(a):
     with open(path, "w") as f:
         f.write("# HBM traffic per dispatch of %s on %s (rocprofv3 --pmc, one counter per run)\n" % (want, cfg_name))
         f.write("# command: %s\n" % a.command)
-        f.write("kernel: %s\n" % (" + ".join(sorted(kn)) if want == "layer_step" else kn[0]))
+        f.write("kernel: %s\n" % (" + ".join(sorted(kn)) if want in ("layer_step", "block_step") else kn[0]))
         f.write("dispatches: %d\n" % len(kf))
         f.write("fetch_kib_per_dispatch: %.1f\n" % mf)
         f.write("write_kib_per_dispatch: %.1f\n" % mw)

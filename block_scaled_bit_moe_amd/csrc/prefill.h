@@ -31,8 +31,15 @@
 // mapping, so every product pairs a weight with its own activation.
 //
 // Activations.  The 64 x 128 bf16 activation tile of a K step is staged in
-// LDS (row stride 272 bytes, so the 16 rows a quarter-wave reads fall on
-// distinct banks), double-buffered, and read by all four waves.
+// LDS, in a ring of stages, and read by all four waves.
+//
+// LDS banks (measured with the bank-conflict counter on the three staged
+// layouts here): a 16-byte read is served 32 lanes at a time across 512 bytes
+// of banks, so the 16 rows of one lane group and the 16 rows of the next must
+// together cover 32 distinct 16-byte slots of a 512-byte window.  The
+// swizzles below XOR a piece index with a row function whose bit 2 is zero:
+// lane groups whose pieces differ in bit 2 then never meet, and within one
+// lane group the function is one-to-one over the rows that share a window.
 #pragma once
 
 #include <type_traits>
@@ -45,6 +52,12 @@ namespace moeq {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4_t;
+
+// Row swizzles (see "LDS banks" above): 256-byte rows (two rows per 512-byte
+// window; one-to-one over the 8 rows of each parity) and 1 KiB rows (one
+// window per 32 pieces; one-to-one over 16 rows).
+__host__ __device__ constexpr int pf_swz256(int r) { return ((r >> 1) & 3) | (r & 8); }
+__host__ __device__ constexpr int pf_swz1k(int r) { return (r & 3) | ((r & 12) << 1); }
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_MB = 64;                   // tokens per block (four 16-row sub-tiles)
@@ -367,8 +380,9 @@ template <int FMT> struct PfUnitLoads { static constexpr int n = Fmt<FMT>::SIX ?
 // waves finished reading one step earlier.
 //
 // Activation stage layout: plane pl (x, or h_hi / h_lo), rows 16 * NSUB of
-// 256 bytes (128 bf16); the 16-byte piece c of row r sits at c ^ (r & 15), so
-// the 16 rows a quarter-wave reads for one MFMA hit 16 different bank groups.
+// 256 bytes (128 bf16); the 16-byte piece c of row r sits at c ^ pf_swz256(r),
+// so the 32 rows-and-pieces that one half-wave reads for an MFMA fill a
+// 512-byte bank window exactly.
 template <int FMT, bool DOWN, int NSUB, int NWAVES, int RG>
 __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2, uint8_t *st3,
                                     const float *s_scale, const int *s_tok, int M,
@@ -407,7 +421,7 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
         const int pl = g / (NSUB * 4);
         const int P = (g % (NSUB * 4)) * 64 + lane;         // 16-byte piece of the plane
         const int row = P >> 4;
-        const int logical = (P & 15) ^ (row & 15);
+        const int logical = (P & 15) ^ pf_swz256(row);
         const int rr = min(row, M - 1);
         row_off[q] = DOWN ? (u32)(p0 + rr) * (u32)a.Imax * 2u : (u32)s_tok[rr] * (u32)H * 2u;
         col_k[q] = (u32)logical * 8u;
@@ -478,7 +492,7 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
         const uint8_t *st = stage(dc);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int piece = ((lg * 4 + s) ^ lr) * 16;
+            const int piece = ((lg * 4 + s) ^ pf_swz256(lr)) * 16;
             bf16x8_t ah[NSUB], al[NSUB];
 #pragma unroll
             for (int m = 0; m < NSUB; ++m) {
@@ -636,8 +650,8 @@ __device__ inline void pf_pin_unit(Unit<FMT> &U) {
 // then streams its weight rows for all H outputs, 32 rows (two 16-row groups)
 // per pass, with PD K steps of weight units in flight in registers and no
 // barrier after the copy -- the weights are private to the wave.  Row r of a
-// plane is 1 KiB; its 16-byte chunk c sits at c ^ (r & 15), so the 16 rows a
-// quarter-wave reads fall on distinct banks.
+// plane is 1 KiB; its 16-byte chunk c sits at c ^ pf_swz1k(r) (inside its
+// 32-chunk window), so a half-wave's 32 reads fall on distinct banks.
 //
 // Each pass ends with its y stores.  On this part vmcnt counts stores as well
 // as loads, and a store may complete before older loads, so the only safe
@@ -671,7 +685,7 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
     const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
 
     // the block's h rows into LDS: copy q of this wave is row (q * 8 + wv) of
-    // the two planes; lane = the row's 16-byte position, holding chunk lane ^ (row & 15)
+    // the two planes; lane = the row's 16-byte position, holding chunk lane ^ pf_swz1k(row)
     {
         const uint64_t bytes = (uint64_t)a.off[a.NS] * a.Imax * 2;
         const __amdgpu_buffer_rsrc_t src[2] = {rsrc_of(a.h_hi, bytes), rsrc_of(a.h_lo, bytes)};
@@ -680,7 +694,7 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
             const int g = q * NWAVES + wv;              // 0 .. 32 NSUB - 1
             constexpr int HALF = CP / 2;                // copies q < HALF are h_hi rows (g < 16 NSUB)
             const int pl = q < HALF ? 0 : 1, row = g - pl * 16 * NSUB;
-            const int c = lane ^ (row & 15);
+            const int c = lane ^ pf_swz1k(row);
             const u32 voff = c * 8 < K ? ((u32)(p0 + min(row, M - 1)) * (u32)a.Imax + (u32)c * 8u) * 2u : 0x7FFFFFF0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(src[pl], (lds_void_t *)(s_h + pl * PF_DR_PLANE + row * 1024), 16,
                                                      voff, 0, 0, 0);
@@ -731,7 +745,7 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
 #pragma unroll
             for (int m = 0; m < NSUB; ++m) {
                 const int row = 16 * m + lr;
-                const uint8_t *ap = s_h + row * 1024 + ((c ^ (row & 15)) << 4);
+                const uint8_t *ap = s_h + row * 1024 + ((c ^ pf_swz1k(row)) << 4);
                 ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap));
                 al[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(ap + PF_DR_PLANE));
             }
