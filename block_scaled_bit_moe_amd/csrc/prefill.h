@@ -642,6 +642,208 @@ __device__ inline void pf_pin_unit(Unit<FMT> &U) {
                      "+v"(U.s));
 }
 
+// Gate | up with bf16 activations on 256-wide K steps (H a multiple of 256;
+// used for the UE8M0 formats): the shape of the scaled kernel below, for the
+// bf16 matrix instructions.  A
+// workgroup of eight waves takes (block of up to 64 tokens, tile of 128
+// intermediate rows); each wave owns 16 gate and the same 16 up rows.  Per K
+// step a lane loads two consecutive units of each of its rows, 8s + 2h and
+// 8s + 2h + 1 (the four lane groups read 64 contiguous code bytes of a row,
+// or 96 for six-bit codes), decodes them as pf_unit_to_b does, and MFMA
+// (t, q) of the step takes weights 8q .. 8q+7 of unit 8s + 2h + t in lane
+// group h: K offsets 64h + 32t + 8q.  The activations are read with the same
+// mapping from a 64 x 512-byte stage (piece 8h + 4t + q of the row, XORed
+// with pf_swz512 of the row).  Two K steps in flight, three stages of 32 KiB,
+// one workgroup per CU.
+constexpr int PF_G2_KS = 256;
+constexpr int PF_G2_ROW = PF_G2_KS * 2;        // bytes per staged bf16 row
+constexpr int PF_G2_NW = 8;
+constexpr int PF_G2_PD = 2;
+// 512-byte rows: one bank window per row; one-to-one over 16 rows, bit 3 clear
+__host__ __device__ constexpr int pf_swz512(int r) { return (r & 7) | ((r & 8) << 1); }
+
+template <int FMT, int NSUB>
+__device__ inline void pf_gu256_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2, const float *s_scale,
+                                     const int *s_tok, int M, int p0, int Is, int n0,
+                                     const uint8_t *const (&rc)[2], const uint8_t *const (&rs)[2]) {
+    constexpr int NW = PF_G2_NW, NB = 2, PD = PF_G2_PD, R = PD + 1;
+    static_assert(R == 3, "three stage objects");
+    constexpr int NDMA = NSUB * 16 * PF_G2_ROW / 1024;  // 1 KiB copies per stage
+    static_assert(NDMA % NW == 0, "copies per wave");
+    constexpr int DPW = NDMA / NW;
+    constexpr int PER_GROUP = DPW + NB * 2 * PfUnitLoads<FMT>::n;
+    constexpr bool WLO = pf_split_w<FMT>();
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lg = lane >> 4, lr = lane & 15;
+    const int H = a.L.H;
+    const int nK = H / PF_G2_KS;
+
+    const __amdgpu_buffer_rsrc_t src = rsrc_of(a.x, (uint64_t)a.T * H * 2);
+    u32 row_off[DPW], col_k[DPW];
+    int dst_off[DPW];
+#pragma unroll
+    for (int q = 0; q < DPW; ++q) {
+        const int g = q * NW + wv;                      // copy index in the stage
+        const int P = g * 64 + lane;                    // 16-byte position in the stage
+        const int row = P >> 5;
+        const int logical = (P & 31) ^ pf_swz512(row);
+        row_off[q] = (u32)s_tok[min(row, M - 1)] * (u32)H * 2u;
+        col_k[q] = (u32)logical * 16u;
+        dst_off[q] = g * 1024;
+    }
+    auto stage = [&](auto sc) -> uint8_t * {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S == 0) return st0;
+        else if constexpr (S == 1) return st1;
+        else return st2;
+    };
+    Unit<FMT> wq[R][NB][2];
+    auto issue = [&](auto sc, int j) {
+        constexpr int S = decltype(sc)::value;
+        uint8_t *st = stage(sc);
+        const int jj = min(j, nK - 1);                  // past the end: the last step again, unused
+        const u32 kb = (u32)jj * PF_G2_ROW;
+#pragma unroll
+        for (int q = 0; q < DPW; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t *)(st + dst_off[q]), 16, row_off[q] + kb + col_k[q],
+                                                     0, 0, 0);
+        const int u0 = jj * 8 + 2 * lg;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            load_unit<FMT>(wq[S][b][0], rc[b], rs[b], u0);
+            load_unit<FMT>(wq[S][b][1], rc[b], rs[b], u0 + 1);
+        }
+    };
+
+    f32x4_t acc[NB][NSUB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) acc[b][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+
+    auto step = [&](auto dc, int it) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + PD) % R;
+        pf_wait_vm<(PD - 1) * PER_GROUP>();             // this wave's step-it loads have landed
+        pf_barrier();                                   // ... and every wave's; stage (it-1) % R is free
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            pf_pin_unit<FMT>(wq[d][b][0]);
+            pf_pin_unit<FMT>(wq[d][b][1]);
+        }
+        issue(std::integral_constant<int, dn>{}, it + PD);
+        asm volatile("" ::: "memory");
+        const uint8_t *st = stage(dc);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x8_t bw[NB][4], bwl[NB][4];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) pf_unit_to_b<FMT>(wq[d][b][t], s_scale, bw[b], bwl[b]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int piece = 8 * lg + 4 * t + q;
+                bf16x8_t ah[NSUB];
+#pragma unroll
+                for (int m = 0; m < NSUB; ++m) {
+                    const int row = 16 * m + lr;
+                    ah[m] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                              st + row * PF_G2_ROW + ((piece ^ pf_swz512(row)) << 4)));
+                }
+#pragma unroll
+                for (int m = 0; m < NSUB; ++m)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bw[b][q], acc[b][m], 0, 0, 0);
+                        if (WLO) acc[b][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bwl[b][q], acc[b][m], 0, 0, 0);
+                    }
+            }
+        }
+    };
+    int it = 0;
+    for (; it + R <= nK; it += R) {
+        step(I0{}, it);
+        step(I1{}, it + 1);
+        step(I2{}, it + 2);
+    }
+    if (it < nK) step(I0{}, it);
+    if (it + 1 < nK) step(I1{}, it + 1);
+    pf_wait_vm<0>();    // the copies issued past the end land before the workgroup's LDS is reused
+
+    // epilogue: lane holds tokens 16m + 4 lg + i, weight row n0 + 16 wv + lr
+    const int nn = n0 + wv * 16 + lr;
+    if (nn >= Is) return;
+#pragma unroll
+    for (int m = 0; m < NSUB; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * m + 4 * lg + i;
+            if (t >= M) continue;
+            const size_t p = (size_t)(p0 + t);
+            const float h = silu_f32(acc[0][m][i]) * acc[1][m][i];
+            const uint16_t hi = f32_to_bf16_rne(h);
+            const uint16_t lo = f32_to_bf16_rne(h - __builtin_bit_cast(float, (u32)hi << 16));
+            a.h_hi[p * a.Imax + nn] = hi;
+            a.h_lo[p * a.Imax + nn] = lo;
+        }
+    }
+}
+
+// One workgroup (eight waves) per (block of up to 64 tokens, tile of 128
+// intermediate rows); the tiles of one block share an XCD.
+template <int FMT>
+__global__ __launch_bounds__(512, 1) void pf_gu256_kernel(PfArgs a, int NT) {
+    constexpr int STAGE_BYTES = PF_MB * PF_G2_ROW;
+    __shared__ __attribute__((aligned(1024))) uint8_t g2_st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t g2_st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t g2_st2[STAGE_BYTES];
+    __shared__ float s_scale[LUT_SCALE];
+    __shared__ int s_tok[PF_MB];
+    const int wid = blockIdx.x;
+    const int win = wid / (8 * NT), q = wid - win * 8 * NT;
+    const int b = win * 8 + (q & 7), nt = q >> 3;
+    if (b >= a.nblk[0]) return;
+    const int packed = a.blk[b];
+    const int slot = packed >> 16, m0 = packed & 0xFFFF;
+    const int E = a.L.E, H = a.L.H;
+    const bool shared = slot == E;
+    const int Is = shared ? a.L.Ish : a.L.I;
+    const int n0 = nt * PF_G2_NW * 16;
+    if (n0 >= Is) return;
+    const int M = min(PF_MB, a.cnt[slot] - m0);
+    const int nsub = (M + 15) >> 4;
+    const int p0 = a.off[slot] + m0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 15;
+    if (Fmt<FMT>::SCALE == SC_E4M3) {   // the other scales are converted arithmetically
+        Luts Lt;
+        Lt.pair = nullptr;
+        Lt.scale = s_scale;
+        build_luts<FMT>(Lt, tid, 64 * PF_G2_NW, false);
+    }
+    if (tid < PF_MB) s_tok[tid] = a.tok[(size_t)slot * a.T + m0 + min(tid, M - 1)];
+
+    using F = Fmt<FMT>;
+    const int64_t crb = F::code_row_bytes(H), srb = F::scale_row_bytes(H);
+    const uint8_t *wc = shared ? a.L.sh13c : a.L.w13c + (size_t)slot * 2 * Is * crb;
+    const uint8_t *ws = shared ? a.L.sh13s : a.L.w13s + (size_t)slot * 2 * Is * srb;
+    const int n = min(n0 + wv * 16 + lr, Is - 1);     // rows past Is: a valid row, result dropped
+    const uint8_t *const rc[2] = {wc + (size_t)n * crb, wc + (size_t)(Is + n) * crb};
+    const uint8_t *const rs[2] = {ws + (size_t)n * srb, ws + (size_t)(Is + n) * srb};
+    __syncthreads();   // s_tok, scale table
+    switch (nsub) {
+        case 1: pf_gu256_main<FMT, 1>(a, g2_st0, g2_st1, g2_st2, s_scale, s_tok, M, p0, Is, n0, rc, rs); break;
+        case 2: pf_gu256_main<FMT, 2>(a, g2_st0, g2_st1, g2_st2, s_scale, s_tok, M, p0, Is, n0, rc, rs); break;
+        case 3: pf_gu256_main<FMT, 3>(a, g2_st0, g2_st1, g2_st2, s_scale, s_tok, M, p0, Is, n0, rc, rs); break;
+        default: pf_gu256_main<FMT, 4>(a, g2_st0, g2_st1, g2_st2, s_scale, s_tok, M, p0, Is, n0, rc, rs); break;
+    }
+}
+
 // Down projection with the block's h resident in LDS.  y = Wd (h_hi + h_lo)
 // has a short K (the intermediate width, 512 here), so a workgroup per (block,
 // tile of rows) would spend most of its life filling its pipeline.  Instead
