@@ -325,3 +325,20 @@ def test_header_word_map_fits_and_does_not_overlap():
     assert not (gu & dn) and not (gu & singles) and not (dn & singles)
     assert max(gu | dn | singles) < WS_HEADER_WORDS
     assert n_groups <= 1024 and WS_GU + 1024 <= WS_DN
+
+
+def test_model_words_are_the_kernels_words():
+    """The header words modelled here are the ones the kernel sources declare."""
+    import os
+    import re
+    src = ""
+    d = os.path.join(os.path.dirname(__file__), "..", "block_scaled_bit_moe_amd", "csrc")
+    for f in ("kernels.h", "prefill.h", "decodeT_impl.h"):
+        src += open(os.path.join(d, f)).read()
+    found = dict((n, int(v)) for n, v in re.findall(r"constexpr (?:int|size_t) (WS_\w+) = (\d+)", src))
+    want = {"WS_ERR": WS_ERR, "WS_EXIT": WS_EXIT, "WS_ARRIVE": WS_ARRIVE, "WS_EPOCH": WS_EPOCH,
+            "WS_PF_ARRIVE": WS_PF_ARRIVE, "WS_ROUTER_ARRIVE": WS_ROUTER_ARRIVE, "WS_GU": WS_GU,
+            "WS_HEADER": WS_HEADER_WORDS * 4}
+    for n, v in want.items():
+        assert found.get(n) == v, (n, found.get(n), v)
+    assert re.search(r"constexpr int WS_DN = 16 \+ 1024;", src) and WS_DN == 16 + 1024
