@@ -66,6 +66,11 @@ def test_e4m3_every_finite_scale(dec):
     y = moeq.dense_gemv_q(W, x, flags=moeq.MOE_OUT_F32 | dec).cpu().numpy()
     want = oracle.tables()["e4m3"][bytes_].astype(np.float32)
     assert np.array_equal(y[0], want) and np.array_equal(y[1], want)
+    # 64 columns (two units per row): the several-token kernel takes it, scale folded into the weights
+    W2 = moeq.QMat(1, rows, 64, dev_u8(np.full((rows, 32), 0x22, np.uint8)),
+                   dev_u8(np.ascontiguousarray(np.stack([bytes_] * 4, axis=1))))
+    y2 = moeq.dense_gemv_q(W2, dev_bf16(_one_hots(64, [0, 63])), flags=moeq.MOE_OUT_F32 | dec).cpu().numpy()
+    assert np.array_equal(y2[0], want) and np.array_equal(y2[1], want)
 
 
 @pytest.mark.parametrize("dec", DECODERS, ids=["lut", "hw"])
@@ -77,6 +82,9 @@ def test_ue8m0_scales(dec):
     codes = np.tile(np.array([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], np.uint8), (rows, cols // 4))
     scales = bytes_.reshape(rows, 1)
     W = moeq.QMat(2, rows, cols, dev_u8(codes), dev_u8(scales))
-    x = dev_bf16(_one_hots(cols, [5]))
+    x = dev_bf16(_one_hots(cols, [5, cols - 1]))     # two tokens: the several-token kernel too
     y = moeq.dense_gemv_q(W, x, flags=moeq.MOE_OUT_F32 | dec).cpu().numpy()
-    assert np.array_equal(y[0], oracle.tables()["ue8m0"][bytes_].astype(np.float32))
+    want = oracle.tables()["ue8m0"][bytes_].astype(np.float32)
+    assert np.array_equal(y[0], want) and np.array_equal(y[1], want)
+    y1 = moeq.dense_gemv_q(W, x[:1], flags=moeq.MOE_OUT_F32 | dec).cpu().numpy()
+    assert np.array_equal(y1[0], want)

@@ -42,3 +42,20 @@ def test_gemv_full_size_sampled():
         y32 = moeq.dense_gemv_q(W, dev_bf16(x), flags=moeq.MOE_OUT_F32).cpu().numpy()
         ref = oracle.gemv(cfg.fmt, cfg.rows, cfg.cols, c, s, x, row_list=rows)
         assert max_rel_err(y32[:, rows], ref) <= PARITY_TOL
+
+
+@pytest.mark.parametrize("fmt,rows,cols,B", [(1, 33000, 256, 3), (2, 1000, 384, 5), (1, 17, 64, 2), (2, 2070, 1152, 8)])
+def test_gemv_matrix_core_tiling(fmt, rows, cols, B):
+    """The several-token kernel's tiling edge cases: more 16-row tiles than a
+    workgroup holds partial sums for (33000 rows: two tile groups on some
+    workgroups), fewer K steps than waves (one or two), a ragged last tile, and
+    fewer tiles than CUs; sampled rows against the oracle."""
+    require_gpu()
+    c, s = synth.matrix(fmt, rows, cols, 13, synth.stream_id(synth.K_W_CODES, rows), synth.stream_id(synth.K_W_SCALES, rows))
+    x = synth.normal_bf16(13, synth.stream_id(synth.K_X, cols), B * cols).reshape(B, cols)
+    W = moeq.QMat(fmt, rows, cols, dev_u8(c), dev_u8(s))
+    y32 = moeq.dense_gemv_q(W, dev_bf16(x), flags=moeq.MOE_OUT_F32).cpu().numpy()
+    sample = np.unique(np.concatenate([np.arange(0, rows, max(1, rows // 300)), np.arange(rows - 40, rows)]))
+    sample = sample[sample >= 0]
+    ref = oracle.gemv(fmt, rows, cols, c, s, x, row_list=sample)
+    assert max_rel_err(y32[:, sample], ref) <= PARITY_TOL
