@@ -53,7 +53,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 def kernel_of(workload, batch=1):
     """The dominant kernel of a workload (the one the roofline is quoted for)."""
     if workload == "dense_gemv_e2m3":
-        return "gemv_reg_kernel" if batch == 1 else "gemv_lds_kernel"
+        return "gemv_reg_kernel" if batch == 1 else "gemv_mfma_kernel"
     return {"wide_decode": "decode1_kernel", "toy_decode": "decode1_kernel",
             "batched_decode": "decodeT_kernel", "prefill": "layer_step",
             "wide_block": "block_step", "batched_block": "block_step"}.get(workload, "kernel")
@@ -100,8 +100,14 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload, batch):
+def traffic_file(workload, batch, fmt=0, act="bf16"):
+    """Summary file of one workload; a format or activation other than the
+    workload's own gets a file of its own (its kernels and bytes differ)."""
     tag = workload if workload != "dense_gemv_e2m3" else "%s_b%d" % (workload, batch)
+    if fmt:
+        tag += "_fmt%d" % fmt
+    if act != "bf16":
+        tag += "_" + act
     return os.path.join(PROFILES, "traffic_%s_%s.txt" % (kernel_of(workload, batch), tag))
 
 
@@ -165,7 +171,7 @@ def traffic_summary(a):
     mf, mw = sum(kf) / len(kf), sum(kw) / len(kw)
     traffic = (mf * ff + mw * wf) * 1024.0
     os.makedirs(PROFILES, exist_ok=True)
-    path = traffic_file(cfg_name, batch)
+    path = traffic_file(cfg_name, batch, a.fmt, a.act)
     with open(path, "w") as f:
         f.write("# HBM traffic per dispatch of %s on %s (rocprofv3 --pmc, one counter per run)\n" % (want, cfg_name))
         f.write("# command: %s\n" % a.command)
@@ -183,10 +189,10 @@ def traffic_summary(a):
     print(open(path).read())
 
 
-def measured_traffic(workload, batch):
+def measured_traffic(workload, batch, fmt=0, act="bf16"):
     """Calibrated HBM bytes per dispatch from the committed summary, or None when
     there is none or the kernels changed since it was taken."""
-    path = traffic_file(workload, batch)
+    path = traffic_file(workload, batch, fmt, act)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -579,7 +585,7 @@ def main():
         cpu = {"value": v_all, "unit": "tokens/s", "cores": omp, "kind": "oracle", "sample": s_all,
                "single_thread": {"value": v_one, "unit": "tokens/s", "cores": 1, "sample": s_one}}
 
-    traffic = measured_traffic(cfg.name, a.batch)
+    traffic = measured_traffic(cfg.name, a.batch, a.fmt, a.act)
     line = {
         "metric": "MoE decode layer tokens/s and effective weight GB/s (% of 8 TB/s HBM)",
         "value": metric_value,

@@ -537,9 +537,14 @@ hipError_t gemv_q(const uint8_t *codes, const uint8_t *scales, int rows, int col
                          void *y, int out_f32, hipStream_t s) {
     const int U = cols / 32, LPR = lanes_per_row(U), Q = (U + LPR - 1) / LPR;
     const bool one = (B == 1);
-    // the matrix-core kernel loads runs of gm_upl units: rows must hold a whole number of them
+    // The matrix-core kernel loads runs of gm_upl units: rows must hold a whole
+    // number of them.  int4 + fp16 weights enter it as two bf16 parts (twice
+    // the instructions, and an fp32 product per weight to split), which only
+    // pays above four tokens (25600 x 5120: B = 2, 4, 8 in 39.3, 40.3, 42.0 us
+    // against 28.5, 37.6, 56.3 us with the dot2 kernel).
     if constexpr (DEC == DEC_HW)
-        if (!one && U % gm_upl<FMT>() == 0) return gemv_mfma_go<FMT>(codes, scales, rows, cols, x, B, y, out_f32, s);
+        if (!one && U % gm_upl<FMT>() == 0 && (FMT != FMT_INT4 || B > 4))
+            return gemv_mfma_go<FMT>(codes, scales, rows, cols, x, B, y, out_f32, s);
 #define GO(QQ)                                                                                    \
     if (Q == QQ) {                                                                                \
         if (one) return gemv_reg_go<FMT, DEC, QQ, 1>(codes, scales, rows, cols, x, B, y, out_f32, s); \
