@@ -43,7 +43,7 @@ constexpr int DT_MAX_GROUPS = DEC_MAX_T * 32 + 1;
 constexpr int DT_HPT = 8;                         // h pieces per thread per read pass (phase C)
 
 // Rows per lane group and item (gate/up: row pairs), so that every lane has
-// several unit loads in flight in each of the two pipeline stages.
+// several unit loads in flight per item.
 __host__ __device__ constexpr int dt_rows_gu(int QG) { return QG >= 2 ? 1 : 2; }
 __host__ __device__ constexpr int dt_rows_dn(int QD) { return QD >= 2 ? 1 : 2; }
 
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                     *reinterpret_cast<uint4 *>(s_buf + u * USx + 16 * t + 4 * v) = val;
                 }
                 __syncthreads();
-                Unit<FMT> un[2][RG][2][QG];
+                Unit<FMT> un[1][RG][2][QG];
                 auto issue = [&](int st, int p) {
 #pragma unroll
                     for (int b = 0; b < RG; ++b) {
@@ -362,18 +362,19 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                         }
                     }
                 };
-                // two items in flight per wave; an item past the end loads the first rows again
+                // one item per wave at a time (the other waves' loads cover the
+                // wait): on the batched layer 0.455 ms against 0.461 with the next
+                // item's loads in flight during the dots (fewer rows open per CU
+                // stream faster; the down phase below keeps two in flight, which
+                // measured faster there).  An item past the end loads the first
+                // rows again.
                 int ia = grab();
                 issue(0, ia);
                 for (;;) {
-                    const int ib = grab();
-                    issue(1, ib);
                     if (ia >= nitem) break;
                     compute(0, ia);
                     ia = grab();
                     issue(0, ia);
-                    if (ib >= nitem) break;
-                    compute(1, ib);
                 }
                 ++nbatch;
             }
