@@ -525,15 +525,27 @@ __global__ __launch_bounds__(DT_THREADS) void decodeT_kernel(DecodeArgs a, DTPla
                         }
                     }
                 };
-                for (;;) {
-                    const int ib = grab();
-                    issue(1, ib);
-                    if (ia >= nitem) break;
-                    compute(0, ia);
-                    ia = grab();
-                    issue(0, ia);
-                    if (ib >= nitem) break;
-                    compute(1, ib);
+                // six-bit codes: one item per wave at a time (0.582 against 0.588 ms
+                // for e2m3 + UE8M0, 0.617 against 0.626 for e2m3 + e4m3); four-bit
+                // codes: two in flight (0.458 against 0.464 ms with one)
+                if constexpr (Fmt<FMT>::SIX) {
+                    for (;;) {
+                        if (ia >= nitem) break;
+                        compute(0, ia);
+                        ia = grab();
+                        issue(0, ia);
+                    }
+                } else {
+                    for (;;) {
+                        const int ib = grab();
+                        issue(1, ib);
+                        if (ia >= nitem) break;
+                        compute(0, ia);
+                        ia = grab();
+                        issue(0, ia);
+                        if (ib >= nitem) break;
+                        compute(1, ib);
+                    }
                 }
                 ++nbatch;
             }
