@@ -66,7 +66,8 @@ constexpr int PF_RG_GU = 1;                 // 16-row groups per wave: gate/up (
 // down: e2m1 takes four (measured: 2 -> 4 took 10 us off the 2,048-token
 // layer); six-bit codes' larger units would spill registers with four
 template <int FMT> constexpr int pf_rg_dn() { return Fmt<FMT>::SIX ? 2 : 4; }
-constexpr int PF_PD = 3;                    // weight units in flight per row group (K steps ahead)
+constexpr int PF_PD = 2;                    // weight units in flight per row group (K steps ahead; three
+                                            // measured 1-3 % slower: fewer rows open per CU)
 constexpr int PF_MAX_K = 32;                // top-k limit of the layer
 
 struct PfArgs {
@@ -273,7 +274,7 @@ template <int FMT> struct PfUnitLoads { static constexpr int n = Fmt<FMT>::SIX ?
 // so the 32 rows-and-pieces that one half-wave reads for an MFMA fill a
 // 512-byte bank window exactly.
 template <int FMT, bool DOWN, int NSUB, int NWAVES, int RG>
-__device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2, uint8_t *st3,
+__device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1, uint8_t *st2,
                                     const float *s_scale, const int *s_tok, int M,
                                     int p0, int K, int N, int n0, const uint8_t *const (&rc)[DOWN ? RG : 2 * RG],
                                     const uint8_t *const (&rs)[DOWN ? RG : 2 * RG]) {
@@ -281,7 +282,7 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
     constexpr int NPL = DOWN ? 2 : 1;
     constexpr int PLANE = NSUB * 16 * 256;                  // bytes per plane of a stage
     constexpr int R = PF_PD + 1;                            // stages in the ring (separate LDS objects)
-    static_assert(R == 4, "four stage objects");
+    static_assert(R == 3, "three stage objects");
     constexpr int NDMA = NSUB * 4 * NPL;                    // 1 KiB copies per stage
     static_assert(NDMA % NWAVES == 0, "copies per wave");
     constexpr int DPW = NDMA / NWAVES;                      // per wave
@@ -323,8 +324,7 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
         constexpr int S = decltype(sc)::value;
         if constexpr (S == 0) return st0;
         else if constexpr (S == 1) return st1;
-        else if constexpr (S == 2) return st2;
-        else return st3;
+        else return st2;
     };
     auto issue_stage = [&](auto sc, int j) {
         uint8_t *st = stage(sc);
@@ -353,16 +353,13 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     // prologue: steps 0 .. PD-1 in flight
     issue_stage(I0{}, 0);
     load_w(wq[0], 0);
     issue_stage(I1{}, 1);
     load_w(wq[1], 1);
-    issue_stage(I2{}, 2);
-    load_w(wq[2], 2);
 
-    // step it uses stage and weight slot it % 4 and refills slot (it + 3) % 4
+    // step it uses stage and weight slot it % 3 and refills slot (it + 2) % 3
     auto step = [&](auto dc, int it) {
         constexpr int d = decltype(dc)::value;
         constexpr int dn = (d + PF_PD) % R;
@@ -409,11 +406,9 @@ __device__ inline void pf_gemm_main(const PfArgs &a, uint8_t *st0, uint8_t *st1,
         step(I0{}, it);
         step(I1{}, it + 1);
         step(I2{}, it + 2);
-        step(I3{}, it + 3);
     }
     if (it < nK) step(I0{}, it);
     if (it + 1 < nK) step(I1{}, it + 1);
-    if (it + 2 < nK) step(I2{}, it + 2);
     // drain the copies issued past the end before the workgroup's LDS is reused
     pf_wait_vm<0>();
 
@@ -457,7 +452,6 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
     __shared__ __attribute__((aligned(1024))) uint8_t pf_st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t pf_st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t pf_st2[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t pf_st3[STAGE_BYTES];
     __shared__ float s_scale[LUT_SCALE];
     __shared__ int s_tok[PF_MB];
 
@@ -512,10 +506,10 @@ __global__ __launch_bounds__(DOWN ? 512 : 256, DOWN ? 1 : 2) void pf_gemm_kernel
     }
     __syncthreads();   // s_tok, scale table
     switch (nsub) {
-        case 1: pf_gemm_main<FMT, DOWN, 1, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
-        case 2: pf_gemm_main<FMT, DOWN, 2, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
-        case 3: pf_gemm_main<FMT, DOWN, 3, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
-        default: pf_gemm_main<FMT, DOWN, 4, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, pf_st3, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        case 1: pf_gemm_main<FMT, DOWN, 1, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        case 2: pf_gemm_main<FMT, DOWN, 2, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        case 3: pf_gemm_main<FMT, DOWN, 3, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
+        default: pf_gemm_main<FMT, DOWN, 4, NWAVES, RG>(a, pf_st0, pf_st1, pf_st2, s_scale, s_tok, M, p0, K, N, n0, rc, rs); break;
     }
 }
 
@@ -895,20 +889,13 @@ __global__ __launch_bounds__(512, 1) void pf_down_res_kernel(PfArgs a) {
     const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
     const uint8_t *wc = shared ? a.L.sh2c : a.L.w2c + (size_t)slot * H * crb;
     const uint8_t *ws = shared ? a.L.sh2s : a.L.w2s + (size_t)slot * H * srb;
-    if (K / PF_KS >= 4) {
-        switch (nsub) {
-            case 1: pf_down_res_main<FMT, 1, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            case 2: pf_down_res_main<FMT, 2, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            case 3: pf_down_res_main<FMT, 3, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            default: pf_down_res_main<FMT, 4, 4>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-        }
-    } else {
-        switch (nsub) {
-            case 1: pf_down_res_main<FMT, 1, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            case 2: pf_down_res_main<FMT, 2, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            case 3: pf_down_res_main<FMT, 3, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-            default: pf_down_res_main<FMT, 4, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-        }
+    // two K steps of weight units in flight (I = 512: 0.423 ms for the step
+    // against 0.429 with four; fewer rows' loads open per CU)
+    switch (nsub) {
+        case 1: pf_down_res_main<FMT, 1, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+        case 2: pf_down_res_main<FMT, 2, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+        case 3: pf_down_res_main<FMT, 3, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+        default: pf_down_res_main<FMT, 4, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
     }
 }
 
