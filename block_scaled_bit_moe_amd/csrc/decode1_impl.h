@@ -3,9 +3,10 @@
 // docs/INTEL.md, "The engine itself on Intel": router_top10, shared_expert).
 //
 // With one token every selected expert serves exactly one row, so the work is
-// static once the token is routed.  One workgroup of 16 waves per CU (a burst
-// of loads streams at the rate of the waves issuing it, so every CU needs
-// many waves, not many loads per wave):
+// static once the token is routed.  One workgroup of 16 waves on each of 7/8
+// of the CUs (a burst of loads streams at the rate of the waves issuing it, so
+// a CU needs many waves, not many loads per wave; and the fewer workgroups the
+// h exchange waits for, the sooner it ends):
 //   gate | up : the layer's P = k*I + Ish (gate row, up row) pairs, routed
 //               experts in rank order then the shared expert, are split into
 //               G equal ranges with even bounds; workgroup w computes range w
