@@ -147,7 +147,7 @@ def traffic_summary(a):
         # a step of several launches (the many-token layer: route, group, gate|up,
         # down, combine; the block: norm, router scores, layer): sum them, per step
         if want == "layer_step":
-            keys, first = ("pf_", "route_kernel", "mx_quant_kernel"), "pf_group"
+            keys, first = ("pf_", "route_kernel", "mx_quant_kernel"), "pf_combine"
         else:
             keys, first = ("rmsnorm_kernel", "router_kernel", "decode1_kernel", "decodeT_kernel"), "rmsnorm_kernel"
 

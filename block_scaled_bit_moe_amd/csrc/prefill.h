@@ -3,12 +3,13 @@
 // With a prompt chunk of 2,048 tokens and top-10 of 512 experts each expert
 // sees about 40 tokens, enough rows for the bf16 matrix instructions to pay
 // (knivesysl "Prompt processing" notes; Strata SYCL port, "MoE prefill").
-// A chunk runs as five launches on one stream:
+// A chunk runs as four launches on one stream:
 //
-//   route    top-k per token (the decode path's routing kernel)
-//   group    per expert slot, the tokens that selected it in ascending token
-//            order; the last workgroup to finish turns the counts into pair
-//            offsets and a list of blocks of up to 64 tokens of one slot
+//   route and group  top-k per token (one wave each), each pick claiming a
+//            place in its expert slot's token list; the last workgroup to
+//            finish turns the counts into pair offsets and a list of blocks
+//            of up to 64 tokens of one slot (calls for one fixed expert:
+//            pf_group_kernel, one workgroup per slot, instead)
 //   gate/up  per (block, tile of 64 intermediate rows): g = Wg x, u = Wu x
 //            on MFMA 16x16x32 bf16 with fp32 accumulation, then
 //            h = silu(g) * u, stored as a bf16 hi + lo pair
@@ -76,14 +77,15 @@ struct PfArgs {
     int T;                    // tokens in the chunk
     int NS;                   // expert slots: E routed, +1 shared (slot E)
     int mode, fixed_e;
-    const int32_t *idx;       // [T][k] (route mode)
-    const float *w;           // [T][k]
+    int32_t *idx;             // [T][k] (route mode; written by pf_route_group_kernel)
+    float *w;                 // [T][k]
+    const float *logits;      // [T][E] router logits of the chunk (route mode)
     int32_t *rank;            // [T][k]: position of the token in its expert's list
     int32_t *cnt;             // [NS]
     int32_t *off;             // [NS + 1]: first pair of each slot
     int32_t *nblk;            // [1]
     int32_t *blk;             // [nblk_max]: slot << 16 | first token of the block
-    int32_t *tok;             // [NS][T]: token ids of each slot, ascending
+    int32_t *tok;             // [NS][T]: token ids of each slot (in claim order when routed)
     uint16_t *h_hi, *h_lo;    // [pairs][Imax] bf16
     float *y;                 // [pairs][H] fp32
     void *out;                // [T][H] bf16 or fp32
@@ -96,6 +98,12 @@ struct PfArgs {
 };
 
 constexpr int WS_PF_ARRIVE = 4;   // header word: group workgroups finished
+// header words WS_PF_CLAIM + s: tokens claimed by slot s while the routing
+// kernel groups them (zero at rest: the last workgroup resets them); above the
+// decode kernels' per-group and per-slice counters
+constexpr int WS_PF_CLAIM = 2048;
+constexpr int PF_MAX_SLOTS = 1024 + 1;   // routed experts (the C ABI's limit) and the shared one
+static_assert(WS_PF_CLAIM + PF_MAX_SLOTS <= (int)(WS_HEADER / 4), "claim words inside the header");
 
 __device__ inline void pf_st_relaxed(int32_t *p, int32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -129,6 +137,37 @@ __device__ inline int pf_block_scan(int v, int *s_tmp, int tid, int &total) {
     total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
     __syncthreads();
     return base + x - v;
+}
+
+// The plan, built by the last workgroup of a grouping launch from the slots'
+// counts (in LDS: s_cnt[s] for every slot): pair offsets and the block list,
+// slot by slot in ascending order; then the arrival counter goes back to zero.
+__device__ inline void pf_build_plan(const PfArgs &a, const int *s_cnt, int *s_tmp, int tid) {
+    const int NS = a.NS;
+    const int per = (NS + PF_THREADS - 1) / PF_THREADS;
+    const int s0 = tid * per;
+    int c_sum = 0, b_sum = 0;
+    for (int s = s0; s < s0 + per && s < NS; ++s) {
+        const int c = s_cnt[s];
+        c_sum += c;
+        b_sum += (c + PF_MB - 1) / PF_MB;
+    }
+    int c_tot, b_tot;
+    int c_base = pf_block_scan(c_sum, s_tmp, tid, c_tot);
+    int b_base = pf_block_scan(b_sum, s_tmp, tid, b_tot);
+    for (int s = s0; s < s0 + per && s < NS; ++s) {
+        const int c = s_cnt[s];
+        a.off[s] = c_base;
+        const int nb = (c + PF_MB - 1) / PF_MB;
+        for (int j = 0; j < nb; ++j) a.blk[b_base + j] = (s << 16) | (j * PF_MB);
+        c_base += c;
+        b_base += nb;
+    }
+    if (tid == 0) {
+        a.off[NS] = c_tot;
+        a.nblk[0] = b_tot;
+        __hip_atomic_store(&a.hdr[WS_PF_ARRIVE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
@@ -199,32 +238,67 @@ __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    // plan: pair offsets and the block list, slot by slot in ascending order
-    const int NS = a.NS;
-    const int per = (NS + PF_THREADS - 1) / PF_THREADS;
-    const int s0 = tid * per;
-    int c_sum = 0, b_sum = 0;
-    for (int s = s0; s < s0 + per && s < NS; ++s) {
-        const int c = pf_ld_relaxed(&a.cnt[s]);
-        c_sum += c;
-        b_sum += (c + PF_MB - 1) / PF_MB;
+    __shared__ int s_cnt[PF_MAX_SLOTS];
+    for (int s = tid; s < a.NS; s += PF_THREADS) s_cnt[s] = pf_ld_relaxed(&a.cnt[s]);
+    __syncthreads();
+    pf_build_plan(a, s_cnt, s_tmp, tid);
+}
+
+// Route and group in one launch (route mode): wave w of a workgroup routes
+// token 4b + w (top-k with ties to the lower index, softmax over the picks),
+// and each of its k picks claims the next place in its expert's token list
+// with a device-scope atomic on that slot's header word.  The places depend
+// on the order in which the claims arrive, so the lists and the pairs' ranks
+// may differ from run to run; the outputs do not: every token's row is
+// multiplied and combined the same way whatever its place in a block (the
+// matrix instructions keep rows apart, and the combine follows rank order).
+// The last workgroup to arrive moves the claims into cnt[] (the shared slot
+// takes every token), resets the claim words and builds the plan.
+template <int PER_LANE>
+__global__ __launch_bounds__(PF_THREADS) void pf_route_group_kernel(PfArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int T = a.T, k = a.L.k, E = a.L.E;
+    __shared__ int s_tmp[4];
+    __shared__ int s_last;
+    int32_t *claim = reinterpret_cast<int32_t *>(a.hdr) + WS_PF_CLAIM;
+    const int t = blockIdx.x * 4 + (tid >> 6);
+    if (t < T) {   // uniform over the wave
+        int e;
+        float wt;
+        route_one_token_wave<PER_LANE>(a.logits + (int64_t)t * E, E, k, lane, e, wt);
+        if (lane < k) {
+            a.idx[(int64_t)t * k + lane] = e;
+            a.w[(int64_t)t * k + lane] = wt;
+            // a token picks a slot at most once, so p < T while the claim words
+            // start at zero; a place past the list (a workspace that was not
+            // zeroed) is compared before any address is formed from it
+            const int p = __hip_atomic_fetch_add(&claim[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (p < T) a.tok[(size_t)e * T + p] = t;
+            a.rank[(int64_t)t * k + lane] = p < T ? p : 0;   // always a place inside the slot
+        }
+        if (lane == 0 && a.NS > E) a.tok[(size_t)E * T + t] = t;
     }
-    int c_tot, b_tot;
-    int c_base = pf_block_scan(c_sum, s_tmp, tid, c_tot);
-    int b_base = pf_block_scan(b_sum, s_tmp, tid, b_tot);
-    for (int s = s0; s < s0 + per && s < NS; ++s) {
-        const int c = pf_ld_relaxed(&a.cnt[s]);
-        a.off[s] = c_base;
-        const int nb = (c + PF_MB - 1) / PF_MB;
-        for (int j = 0; j < nb; ++j) a.blk[b_base + j] = (s << 16) | (j * PF_MB);
-        c_base += c;
-        b_base += nb;
-    }
+    __syncthreads();   // (with every load and store of the workgroup complete)
     if (tid == 0) {
-        a.off[NS] = c_tot;
-        a.nblk[0] = b_tot;
-        __hip_atomic_store(&a.hdr[WS_PF_ARRIVE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const u32 prev = __hip_atomic_fetch_add(&a.hdr[WS_PF_ARRIVE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.x - 1u) ? 1 : 0;
     }
+    __syncthreads();
+    if (!s_last) return;
+    __shared__ int s_cnt[PF_MAX_SLOTS];
+    for (int s = tid; s < a.NS; s += PF_THREADS) {
+        int c = (s == E) ? T : pf_ld_relaxed(&claim[s]);
+        if (c < 0 || c > T) {   // claims past the list: reported, the count kept inside it
+            pf_st_relaxed(reinterpret_cast<int32_t *>(&a.hdr[WS_ERR]), 1);
+            c = c < 0 ? 0 : T;
+        }
+        s_cnt[s] = c;
+        a.cnt[s] = c;
+        pf_st_relaxed(&claim[s], 0);
+    }
+    __syncthreads();
+    pf_build_plan(a, s_cnt, s_tmp, tid);
 }
 
 // Weight units of one K step for the NB row groups of a lane.  Addresses are

@@ -1,5 +1,5 @@
 // prefill.hip -- host side of the many-token MoE layer: workspace layout,
-// chunking of the tokens and the five launches per chunk.
+// chunking of the tokens and the launches per chunk.
 #include "prefill.h"
 
 namespace moeq {
@@ -61,7 +61,18 @@ static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     const int rows_gu = 4 * 16 * PF_RG_GU, rows_dn = 8 * 16 * pf_rg_dn<FMT>();   // weight rows per workgroup
     const int nt_gu = (Imax + rows_gu - 1) / rows_gu;
     const int nt_dn = (p.L.H + rows_dn - 1) / rows_dn;
-    hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
+    if (p.mode == MODE_ROUTE) {
+        // route and group: one wave per token, the last workgroup builds the plan
+        const dim3 grid((p.T + 3) / 4), block(PF_THREADS);
+        const int E = p.L.E;
+        if (E <= 64) hipLaunchKernelGGL(pf_route_group_kernel<1>, grid, block, 0, s, p);
+        else if (E <= 128) hipLaunchKernelGGL(pf_route_group_kernel<2>, grid, block, 0, s, p);
+        else if (E <= 256) hipLaunchKernelGGL(pf_route_group_kernel<4>, grid, block, 0, s, p);
+        else if (E <= 512) hipLaunchKernelGGL(pf_route_group_kernel<8>, grid, block, 0, s, p);
+        else hipLaunchKernelGGL(pf_route_group_kernel<16>, grid, block, 0, s, p);
+    } else {
+        hipLaunchKernelGGL(pf_group_kernel, dim3(p.NS), dim3(PF_THREADS), 0, s, p);
+    }
     // gate | up: MX activations on MX weights take the scaled matrix cores;
     // otherwise 256-wide K steps where H allows, else 128-wide
     const int nt_g2 = (Imax + PF_G2_NW * 16 - 1) / (PF_G2_NW * 16);
@@ -137,10 +148,7 @@ hipError_t launch_prefill(const DecodeArgs &a, hipStream_t s) {
                 p.x = xd;
             }
         }
-        if (a.mode == MODE_ROUTE) {
-            hipError_t e = launch_route(a.logits + (size_t)c0 * L.E, Tc, L.E, L.k, idx, w, s);
-            if (e != hipSuccess) return e;
-        }
+        p.logits = a.mode == MODE_ROUTE ? a.logits + (size_t)c0 * L.E : nullptr;
         hipError_t e;
         switch (L.fmt) {
             case FMT_E2M1: e = pf_chunk<FMT_E2M1>(p, l, s); break;

@@ -14,6 +14,11 @@ Protocols modelled:
   arrival   -- every workgroup publishes its result and adds one to a counter;
                the one that sees N - 1 reads all results and resets the
                counter (the prefill grouping kernel, the fused router top-k);
+  claim     -- the prefill's fused routing and grouping: each token's picks
+               claim places in their slots with atomic adds on per-slot claim
+               words, every workgroup arrives, and the last one reads the
+               claims as the counts and resets the claim words and the
+               arrival counter;
   exit      -- items in a static order, a bounded wait per dependent item that
                on expiry raises the error word and carries on, and an exit
                counter whose last arriver resets every per-call counter (the
@@ -45,6 +50,7 @@ import pytest
 # csrc/prefill.h; the general decode kernel's per-group and per-slice counters
 WS_ERR, WS_EXIT, WS_ARRIVE, WS_EPOCH, WS_PF_ARRIVE, WS_ROUTER_ARRIVE = 0, 1, 2, 3, 4, 5
 WS_GU, WS_DN = 16, 16 + 1024
+WS_PF_CLAIM, PF_MAX_SLOTS = 2048, 1024 + 1    # claim word of slot s: WS_PF_CLAIM + s
 WS_HEADER_WORDS = 16384 // 4
 DEC_MAX_DIM, DEC_S2, DEC_MAX_T, MAX_TOPK = 8192, 64, 16, 32
 
@@ -201,14 +207,54 @@ def ticket_call(mem, call, G, n_gu, n_dn, expire, fixed):
     return [wg(w) for w in range(G)]
 
 
+def claim_call(mem, call, G, expire, n_slots=5, tokens_per_wg=2, picks=2):
+    """Workgroup w routes tokens 2w, 2w + 1; pick r of token t is slot
+    (t + 1 + 2r) % n_slots (distinct per token).  A claimed place at or past
+    the token count is recorded as a bad index (the kernel compares it before
+    forming an address); the last arriver checks the counts and that no place
+    was handed out twice, then resets every claim word and the counter."""
+    T = G * tokens_per_wg
+    slot_of = lambda t, r: (t + 1 + 2 * r) % n_slots
+    if mem.ld(WS_PF_ARRIVE) or any(mem.ld(WS_PF_CLAIM + s) for s in range(n_slots)):
+        call.stale_start.append(-1)
+    places = {}
+
+    def wg(w):
+        for j in range(tokens_per_wg):
+            t = w * tokens_per_wg + j
+            for r in range(picks):
+                s = slot_of(t, r)
+                p = mem.add(WS_PF_CLAIM + s, 1)
+                yield
+                if p >= T:
+                    call.bad_index.append(p)
+                    continue
+                places[(s, p)] = places.get((s, p), 0) + 1
+                call.done[t * picks + r] += 1
+        prev = mem.add(WS_PF_ARRIVE, 1)
+        yield
+        if prev == G - 1:
+            counts = [mem.ld(WS_PF_CLAIM + s) for s in range(n_slots)]
+            want = [sum(slot_of(t, r) == s for t in range(T) for r in range(picks)) for s in range(n_slots)]
+            if counts != want or any(v != 1 for v in places.values()):
+                call.wrong_last = True
+            for s in range(n_slots):
+                mem.st(WS_PF_CLAIM + s, 0)
+                yield
+            mem.st(WS_PF_ARRIVE, 0)
+            yield
+    return [wg(w) for w in range(G)]
+
+
 PROTOCOLS = {
     "arrival": lambda mem, call, G, expire: arrival_call(mem, call, G, WS_PF_ARRIVE, expire),
     "router_arrival": lambda mem, call, G, expire: arrival_call(mem, call, G, WS_ROUTER_ARRIVE, expire),
     "exit": lambda mem, call, G, expire: exit_call(mem, call, G, 6, 4, expire),
     "ticket": lambda mem, call, G, expire: ticket_call(mem, call, G, 6, 4, expire, False),
     "ticket_fixed": lambda mem, call, G, expire: ticket_call(mem, call, G, 6, 4, expire, True),
+    "claim": lambda mem, call, G, expire: claim_call(mem, call, G, expire),
 }
-N_ITEMS = {"arrival": None, "router_arrival": None, "exit": 10, "ticket": 10, "ticket_fixed": 10}
+N_ITEMS = {"arrival": None, "router_arrival": None, "exit": 10, "ticket": 10, "ticket_fixed": 10, "claim": 32}
 
 
 def one_call(name, mem, rng, G=8, expire=False):
@@ -236,7 +282,7 @@ SCENARIOS = {
 
 
 @pytest.mark.parametrize("scenario", sorted(SCENARIOS))
-@pytest.mark.parametrize("name", ["arrival", "router_arrival", "exit", "ticket_fixed"])
+@pytest.mark.parametrize("name", ["arrival", "router_arrival", "exit", "claim", "ticket_fixed"])
 def test_protocols_in_use_hold(name, scenario):
     for seed in range(40):
         rng = random.Random(seed)
@@ -253,7 +299,7 @@ def test_interleaved_kernels_share_one_header():
         rng = random.Random(seed)
         mem = Mem()
         for _ in range(3):
-            for name in rng.sample(["arrival", "router_arrival", "exit", "ticket_fixed"], 4):
+            for name in rng.sample(["arrival", "router_arrival", "exit", "claim", "ticket_fixed"], 5):
                 call = one_call(name, mem, rng, expire=rng.random() < 0.3)
                 assert not call.stale_start and not call.bad_index and not call.wrong_last, (name, seed)
 
@@ -323,7 +369,9 @@ def test_header_word_map_fits_and_does_not_overlap():
     singles = {WS_ERR, WS_EXIT, WS_ARRIVE, WS_EPOCH, WS_PF_ARRIVE, WS_ROUTER_ARRIVE}
     assert len(singles) == 6
     assert not (gu & dn) and not (gu & singles) and not (dn & singles)
-    assert max(gu | dn | singles) < WS_HEADER_WORDS
+    claims = set(range(WS_PF_CLAIM, WS_PF_CLAIM + PF_MAX_SLOTS))
+    assert not (claims & (gu | dn | singles))
+    assert max(gu | dn | singles | claims) < WS_HEADER_WORDS
     assert n_groups <= 1024 and WS_GU + 1024 <= WS_DN
 
 
@@ -338,6 +386,7 @@ def test_model_words_are_the_kernels_words():
     found = dict((n, int(v)) for n, v in re.findall(r"constexpr (?:int|size_t) (WS_\w+) = (\d+)", src))
     want = {"WS_ERR": WS_ERR, "WS_EXIT": WS_EXIT, "WS_ARRIVE": WS_ARRIVE, "WS_EPOCH": WS_EPOCH,
             "WS_PF_ARRIVE": WS_PF_ARRIVE, "WS_ROUTER_ARRIVE": WS_ROUTER_ARRIVE, "WS_GU": WS_GU,
+            "WS_PF_CLAIM": WS_PF_CLAIM,
             "WS_HEADER": WS_HEADER_WORDS * 4}
     for n, v in want.items():
         assert found.get(n) == v, (n, found.get(n), v)

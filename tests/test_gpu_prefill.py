@@ -179,3 +179,26 @@ def test_one_workspace_for_both_paths():
         print("mixed workspace T", T, flush=True)
         x, l = synth.hidden_states(cfg, tokens=T, sub=sub), synth.router_logits(cfg, tokens=T, sub=sub)
         _check(cfg, x, l, *_run(cfg, x, l, ws=ws))
+
+
+@pytest.mark.parametrize("cfg", [PF_SHARED, PF_CHUNKED], ids=lambda c: c.name)
+def test_prefill_claim_words_back_at_zero(cfg):
+    """Routed calls group their tokens through per-slot claim words in the
+    workspace header (places in the expert lists follow the order the claims
+    arrive in); after every call, single chunk or several, the last workgroup
+    has reset them and the arrival counter, so consecutive calls on one
+    workspace agree bitwise and the status stays clean."""
+    require_gpu()
+    L = _layer(cfg)
+    T = cfg.tokens
+    ws = moeq.workspace(L, T)
+    x, l = synth.hidden_states(cfg, tokens=T, sub=31), synth.router_logits(cfg, tokens=T, sub=31)
+    outs = []
+    for _ in range(3):
+        _, _, o32, _ = _run(cfg, x, l, ws=ws)
+        hdr = ws[:16384].view(torch.int32).cpu().numpy()
+        ns = cfg.experts + (1 if cfg.shared_inter else 0)
+        assert not hdr[2048:2048 + ns].any() and hdr[4] == 0
+        assert moeq.moe_workspace_status(ws) == moeq.MOE_OK
+        outs.append(o32)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
