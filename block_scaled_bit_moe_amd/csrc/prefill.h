@@ -120,7 +120,9 @@ __device__ inline bool pf_slot_identity(const PfArgs &a, int slot) {
     return a.mode == MODE_FIXED_ROUTED ? slot == a.fixed_e : slot == a.L.E;
 }
 
-// Exclusive scan over the 256 threads of a block (values in v, total returned).
+// Exclusive scan over the NT threads of a block (values in v, total returned;
+// s_tmp holds NT / 64 ints).
+template <int NT>
 __device__ inline int pf_block_scan(int v, int *s_tmp, int tid, int &total) {
     const int lane = tid & 63, wv = tid >> 6;
     // inclusive scan within the wave
@@ -133,8 +135,12 @@ __device__ inline int pf_block_scan(int v, int *s_tmp, int tid, int &total) {
     if (lane == 63) s_tmp[wv] = x;
     __syncthreads();
     int base = 0;
-    for (int i = 0; i < wv; ++i) base += s_tmp[i];
-    total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        if (i < wv) base += s_tmp[i];
+        total += s_tmp[i];
+    }
     __syncthreads();
     return base + x - v;
 }
@@ -142,9 +148,10 @@ __device__ inline int pf_block_scan(int v, int *s_tmp, int tid, int &total) {
 // The plan, built by the last workgroup of a grouping launch from the slots'
 // counts (in LDS: s_cnt[s] for every slot): pair offsets and the block list,
 // slot by slot in ascending order; then the arrival counter goes back to zero.
+template <int NT>
 __device__ inline void pf_build_plan(const PfArgs &a, const int *s_cnt, int *s_tmp, int tid) {
     const int NS = a.NS;
-    const int per = (NS + PF_THREADS - 1) / PF_THREADS;
+    const int per = (NS + NT - 1) / NT;
     const int s0 = tid * per;
     int c_sum = 0, b_sum = 0;
     for (int s = s0; s < s0 + per && s < NS; ++s) {
@@ -153,8 +160,8 @@ __device__ inline void pf_build_plan(const PfArgs &a, const int *s_cnt, int *s_t
         b_sum += (c + PF_MB - 1) / PF_MB;
     }
     int c_tot, b_tot;
-    int c_base = pf_block_scan(c_sum, s_tmp, tid, c_tot);
-    int b_base = pf_block_scan(b_sum, s_tmp, tid, b_tot);
+    int c_base = pf_block_scan<NT>(c_sum, s_tmp, tid, c_tot);
+    int b_base = pf_block_scan<NT>(b_sum, s_tmp, tid, b_tot);
     for (int s = s0; s < s0 + per && s < NS; ++s) {
         const int c = s_cnt[s];
         a.off[s] = c_base;
@@ -241,11 +248,11 @@ __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
     __shared__ int s_cnt[PF_MAX_SLOTS];
     for (int s = tid; s < a.NS; s += PF_THREADS) s_cnt[s] = pf_ld_relaxed(&a.cnt[s]);
     __syncthreads();
-    pf_build_plan(a, s_cnt, s_tmp, tid);
+    pf_build_plan<PF_THREADS>(a, s_cnt, s_tmp, tid);
 }
 
-// Route and group in one launch (route mode): wave w of a workgroup routes
-// token 4b + w (top-k with ties to the lower index, softmax over the picks),
+// Route and group in one launch (route mode): wave w of workgroup b routes
+// token 16b + w (top-k with ties to the lower index, softmax over the picks),
 // and each of its k picks claims the next place in its expert's token list
 // with a device-scope atomic on that slot's header word.  The places depend
 // on the order in which the claims arrive, so the lists and the pairs' ranks
@@ -253,15 +260,17 @@ __global__ __launch_bounds__(PF_THREADS) void pf_group_kernel(PfArgs a) {
 // multiplied and combined the same way whatever its place in a block (the
 // matrix instructions keep rows apart, and the combine follows rank order).
 // The last workgroup to arrive moves the claims into cnt[] (the shared slot
-// takes every token), resets the claim words and builds the plan.
+// takes every token), resets the claim words and builds the plan.  Sixteen
+// waves to a workgroup keep the arrivals on the one counter word few.
+constexpr int PF_RG_THREADS = 1024;
 template <int PER_LANE>
-__global__ __launch_bounds__(PF_THREADS) void pf_route_group_kernel(PfArgs a) {
+__global__ __launch_bounds__(PF_RG_THREADS) void pf_route_group_kernel(PfArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int T = a.T, k = a.L.k, E = a.L.E;
-    __shared__ int s_tmp[4];
+    __shared__ int s_tmp[PF_RG_THREADS / 64];
     __shared__ int s_last;
     int32_t *claim = reinterpret_cast<int32_t *>(a.hdr) + WS_PF_CLAIM;
-    const int t = blockIdx.x * 4 + (tid >> 6);
+    const int t = blockIdx.x * (PF_RG_THREADS / 64) + (tid >> 6);
     if (t < T) {   // uniform over the wave
         int e;
         float wt;
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(PF_THREADS) void pf_route_group_kernel(PfArgs a) {
     __syncthreads();
     if (!s_last) return;
     __shared__ int s_cnt[PF_MAX_SLOTS];
-    for (int s = tid; s < a.NS; s += PF_THREADS) {
+    for (int s = tid; s < a.NS; s += PF_RG_THREADS) {
         int c = (s == E) ? T : pf_ld_relaxed(&claim[s]);
         if (c < 0 || c > T) {   // claims past the list: reported, the count kept inside it
             pf_st_relaxed(reinterpret_cast<int32_t *>(&a.hdr[WS_ERR]), 1);
@@ -298,7 +307,7 @@ __global__ __launch_bounds__(PF_THREADS) void pf_route_group_kernel(PfArgs a) {
         pf_st_relaxed(&claim[s], 0);
     }
     __syncthreads();
-    pf_build_plan(a, s_cnt, s_tmp, tid);
+    pf_build_plan<PF_RG_THREADS>(a, s_cnt, s_tmp, tid);
 }
 
 // Weight units of one K step for the NB row groups of a lane.  Addresses are

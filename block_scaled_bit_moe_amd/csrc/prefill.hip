@@ -63,7 +63,8 @@ static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     const int nt_dn = (p.L.H + rows_dn - 1) / rows_dn;
     if (p.mode == MODE_ROUTE) {
         // route and group: one wave per token, the last workgroup builds the plan
-        const dim3 grid((p.T + 3) / 4), block(PF_THREADS);
+        constexpr int tpw = PF_RG_THREADS / 64;   // tokens per workgroup
+        const dim3 grid((p.T + tpw - 1) / tpw), block(PF_RG_THREADS);
         const int E = p.L.E;
         if (E <= 64) hipLaunchKernelGGL(pf_route_group_kernel<1>, grid, block, 0, s, p);
         else if (E <= 128) hipLaunchKernelGGL(pf_route_group_kernel<2>, grid, block, 0, s, p);
