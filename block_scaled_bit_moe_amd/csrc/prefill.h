@@ -801,10 +801,10 @@ __global__ __launch_bounds__(512, 1) void pf_gu256_kernel(PfArgs a, int NT) {
 // Down projection with the block's h resident in LDS.  y = Wd (h_hi + h_lo)
 // has a short K (the intermediate width, 512 here), so a workgroup per (block,
 // tile of rows) would spend most of its life filling its pipeline.  Instead
-// one workgroup of eight waves takes a whole block: it copies the block's
-// h_hi and h_lo rows into LDS once (64 rows x 1 KiB per plane), and every wave
-// then streams its weight rows for all H outputs, 32 rows (two 16-row groups)
-// per pass, with PD K steps of weight units in flight in registers and no
+// one workgroup of eight waves takes a run of passes of a block: it copies the
+// block's h_hi and h_lo rows into LDS once (64 rows x 1 KiB per plane), and
+// every wave then streams its weight rows for the run's outputs, 32 rows (two
+// 16-row groups) per pass, with PD K steps of weight units in flight in registers and no
 // barrier after the copy -- the weights are private to the wave.  Row r of a
 // plane is 1 KiB; its 16-byte chunk c sits at c ^ pf_swz1k(r) (inside its
 // 32-chunk window), so a half-wave's 32 reads fall on distinct banks.
@@ -823,7 +823,7 @@ constexpr int PF_DR_PLANE = PF_MB * PF_DR_KMAX * 2;
 
 template <int FMT, int NSUB, int PD>
 __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const float *s_scale, int M, int p0, int K,
-                                        const uint8_t *wc, const uint8_t *ws) {
+                                        const uint8_t *wc, const uint8_t *ws, int ps_lo, int ps_hi) {
     constexpr int NWAVES = 8, RG = PF_DR_RG, R = PD + 1;
     constexpr int PER_GROUP = RG * PfUnitLoads<FMT>::n;
     constexpr int T0 = (PD - 1) * PER_GROUP;            // loads younger than a step's group
@@ -835,8 +835,7 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
     const int H = a.L.H;
     const int nK = K / PF_KS;                           // K steps per pass (>= PD)
     constexpr int ROWS = NWAVES * RG * 16;              // rows per pass
-    const int npass = (H + ROWS - 1) / ROWS;
-    const int nstep = npass * nK;
+    const int nstep = (ps_hi - ps_lo) * nK;             // passes ps_lo .. ps_hi - 1 of the block
     using F = Fmt<FMT>;
     const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
 
@@ -863,7 +862,7 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
     Unit<FMT> wq[R][RG];
     auto load_w = [&](Unit<FMT> (&U)[RG], int f) {
         const int ff = min(f, nstep - 1);
-        const int ps = ff / nK, j = ff - ps * nK;
+        const int ps = ps_lo + ff / nK, j = ff - (ps - ps_lo) * nK;
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
             const int n = min(ps * ROWS + wv * 16 * RG + 16 * g + lr, H - 1);
@@ -883,10 +882,10 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
     auto step = [&](auto dc, int f) {
         constexpr int d = decltype(dc)::value;
         constexpr int dn = (d + PD) % R;
-        const int ps = f / nK, j = f - ps * nK;
+        const int ps = ps_lo + f / nK, j = f - (ps - ps_lo) * nK;
         // step f's units have landed (the first step of a pass: waited for
         // before the previous pass's stores)
-        if (!(ps > 0 && j == 0)) pf_wait_vm<T0>();
+        if (!(ps > ps_lo && j == 0)) pf_wait_vm<T0>();
 #pragma unroll
         for (int g = 0; g < RG; ++g) pf_pin_unit<FMT>(wq[d][g]);
         bf16x8_t bw[RG][4], bwl[RG][4];
@@ -946,21 +945,22 @@ __device__ inline void pf_down_res_main(const PfArgs &a, uint8_t *s_h, const flo
     pf_wait_vm<0>();    // the loads issued past the end land before the wave exits
 }
 
-// One workgroup (eight waves) per block of up to 64 tokens.
+// Down with the h rows resident: a persistent grid of eight-wave workgroups
+// (one per CU) shares out the passes of every block (ROWS output rows each)
+// evenly, in block order, so no CU idles while the last blocks run.  A
+// workgroup whose passes span several blocks copies each block's h rows into
+// LDS when it reaches it.  Every pass of a block computes all K for its rows,
+// so the results do not depend on how the passes are shared out.
 template <int FMT>
 __global__ __launch_bounds__(512, 1) void pf_down_res_kernel(PfArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_h[2 * PF_DR_PLANE];
     __shared__ float s_scale[LUT_SCALE];
-    const int b = blockIdx.x;
-    if (b >= a.nblk[0]) return;
-    const int packed = a.blk[b];
-    const int slot = packed >> 16, m0 = packed & 0xFFFF;
     const int E = a.L.E, H = a.L.H;
-    const bool shared = slot == E;
-    const int K = shared ? a.L.Ish : a.L.I;
-    const int M = min(PF_MB, a.cnt[slot] - m0);
-    const int nsub = (M + 15) >> 4;
-    const int p0 = a.off[slot] + m0;
+    constexpr int ROWS = 8 * PF_DR_RG * 16;
+    const int npass = (H + ROWS - 1) / ROWS;
+    const int64_t total = (int64_t)a.nblk[0] * npass;
+    const int q0 = (int)(total * blockIdx.x / gridDim.x), q1 = (int)(total * (blockIdx.x + 1) / gridDim.x);
+    if (q0 >= q1) return;
     if (Fmt<FMT>::SCALE == SC_E4M3) {   // the other scales are converted arithmetically
         Luts Lt;
         Lt.pair = nullptr;
@@ -969,16 +969,29 @@ __global__ __launch_bounds__(512, 1) void pf_down_res_kernel(PfArgs a) {
         __syncthreads();
     }
     using F = Fmt<FMT>;
-    const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
-    const uint8_t *wc = shared ? a.L.sh2c : a.L.w2c + (size_t)slot * H * crb;
-    const uint8_t *ws = shared ? a.L.sh2s : a.L.w2s + (size_t)slot * H * srb;
-    // two K steps of weight units in flight (I = 512: 0.423 ms for the step
-    // against 0.429 with four; fewer rows' loads open per CU)
-    switch (nsub) {
-        case 1: pf_down_res_main<FMT, 1, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-        case 2: pf_down_res_main<FMT, 2, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-        case 3: pf_down_res_main<FMT, 3, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
-        default: pf_down_res_main<FMT, 4, 2>(a, s_h, s_scale, M, p0, K, wc, ws); break;
+    for (int q = q0; q < q1;) {
+        const int b = q / npass, ps_lo = q - b * npass;
+        const int ps_hi = min(npass, ps_lo + (q1 - q));
+        const int packed = a.blk[b];
+        const int slot = packed >> 16, m0 = packed & 0xFFFF;
+        const bool shared = slot == E;
+        const int K = shared ? a.L.Ish : a.L.I;
+        const int M = min(PF_MB, a.cnt[slot] - m0);
+        const int nsub = (M + 15) >> 4;
+        const int p0 = a.off[slot] + m0;
+        const int64_t crb = F::code_row_bytes(K), srb = F::scale_row_bytes(K);
+        const uint8_t *wc = shared ? a.L.sh2c : a.L.w2c + (size_t)slot * H * crb;
+        const uint8_t *ws = shared ? a.L.sh2s : a.L.w2s + (size_t)slot * H * srb;
+        if (q != q0) __syncthreads();   // every wave is done with the previous block's h rows
+        // two K steps of weight units in flight (I = 512: 0.423 ms for the step
+        // against 0.429 with four; fewer rows' loads open per CU)
+        switch (nsub) {
+            case 1: pf_down_res_main<FMT, 1, 2>(a, s_h, s_scale, M, p0, K, wc, ws, ps_lo, ps_hi); break;
+            case 2: pf_down_res_main<FMT, 2, 2>(a, s_h, s_scale, M, p0, K, wc, ws, ps_lo, ps_hi); break;
+            case 3: pf_down_res_main<FMT, 3, 2>(a, s_h, s_scale, M, p0, K, wc, ws, ps_lo, ps_hi); break;
+            default: pf_down_res_main<FMT, 4, 2>(a, s_h, s_scale, M, p0, K, wc, ws, ps_lo, ps_hi); break;
+        }
+        q += ps_hi - ps_lo;
     }
 }
 

@@ -1,5 +1,7 @@
 // prefill.hip -- host side of the many-token MoE layer: workspace layout,
 // chunking of the tokens and the launches per chunk.
+#include <algorithm>
+
 #include "prefill.h"
 
 namespace moeq {
@@ -95,8 +97,15 @@ static hipError_t pf_chunk(const PfArgs &p, const PfLayout &l, hipStream_t s) {
     // down: the h-resident kernel when every expert's K fits its LDS tile
     const bool res = p.L.I % PF_KS == 0 && p.L.I >= 2 * PF_KS && p.L.I <= PF_DR_KMAX &&
                      (p.L.Ish == 0 || (p.L.Ish % PF_KS == 0 && p.L.Ish >= 2 * PF_KS && p.L.Ish <= PF_DR_KMAX));
-    if (res) hipLaunchKernelGGL((pf_down_res_kernel<FMT>), dim3(l.nblk_max), dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
+    if (res) {
+        // persistent: one workgroup per CU, the passes of all blocks shared out evenly
+        const int npass = (p.L.H + 8 * PF_DR_RG * 16 - 1) / (8 * PF_DR_RG * 16);
+        const int64_t most = (int64_t)l.nblk_max * npass;
+        const int G = (int)std::min<int64_t>(most, cached_cus());
+        hipLaunchKernelGGL((pf_down_res_kernel<FMT>), dim3(G), dim3(512), 0, s, p);
+    }
+    else
+        hipLaunchKernelGGL((pf_gemm_kernel<FMT, true>), dim3(l.nblk_max * nt_dn), dim3(512), 0, s, p, nt_dn);
     hipLaunchKernelGGL(pf_combine_kernel, dim3(p.T), dim3(PF_THREADS), 0, s, p);
     return hipGetLastError();
 }
