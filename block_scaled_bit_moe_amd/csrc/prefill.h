@@ -41,6 +41,10 @@
 // swizzles below XOR a piece index with a row function whose bit 2 is zero:
 // lane groups whose pieces differ in bit 2 then never meet, and within one
 // lane group the function is one-to-one over the rows that share a window.
+// (The resident-down, 256-wide and MX tiles count no conflicts this way; the
+// 128-wide gate/up kernel still counts them on about half of its LDS cycles,
+// unchanged by a swizzle that is conflict-free under every lane grouping that
+// fits the other tiles' counts, so their source there is not its A reads.)
 #pragma once
 
 #include <type_traits>
