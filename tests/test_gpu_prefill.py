@@ -33,6 +33,10 @@ CFGS = [PF_SMALL, PF_SHARED, PF_E2M3]
 # with two blocks (up to 64 tokens and a ragged rest), every weight format
 PF_RES = [MoEConfig("pf_res_f%d" % f, tokens=150, hidden=768, experts=6, top_k=2, inter=512, shared_inter=384,
                     fmt=f) for f in (1, 2, 3, 4, 5)]
+# the resident down projection's persistent grid: more passes (blocks x
+# ceil(H / 256)) than CUs, so workgroups take runs of passes that start inside
+# a block and cross into the next; H = 1152 ends in a half-empty pass
+PF_RES_WIDE = MoEConfig("pf_res_wide", tokens=1024, hidden=1152, experts=8, top_k=4, inter=256, shared_inter=256)
 _layers = {}
 
 
@@ -78,6 +82,23 @@ def test_prefill_resident_down(cfg):
     print("prefill resident down", cfg.name, flush=True)
     x, l = synth.hidden_states(cfg), synth.router_logits(cfg)
     _check(cfg, x, l, *_run(cfg, x, l))
+
+
+def test_prefill_resident_down_runs_of_passes():
+    """About 85 blocks of 5 passes each, shared out over the CUs: every
+    token's output against the oracle on 128 tokens spread over the call
+    (each block holds tokens among them), the bf16 output bit for bit."""
+    require_gpu()
+    cfg = PF_RES_WIDE
+    print("prefill resident down, runs of passes", flush=True)
+    x, l = synth.hidden_states(cfg, sub=41), synth.router_logits(cfg, sub=41)
+    idx, w, out32, out16 = _run(cfg, x, l)
+    rows = np.arange(3, cfg.tokens, 8)
+    ridx, rw, ref = oracle_layer(cfg, x[rows], l[rows])
+    assert np.array_equal(idx[rows], ridx)
+    assert np.allclose(w[rows], rw, rtol=1e-6, atol=0)
+    assert max_rel_err(out32.cpu().numpy()[rows], ref) <= PARITY_TOL
+    assert np.array_equal(host_bf16(out16), bf16_rne_of_f32(out32))
 
 
 @pytest.mark.parametrize("T", [17, 64, 65, 130])
