@@ -10,11 +10,15 @@
 //            finish turns the counts into pair offsets and a list of blocks
 //            of up to 64 tokens of one slot (calls for one fixed expert:
 //            pf_group_kernel, one workgroup per slot, instead)
-//   gate/up  per (block, tile of 64 intermediate rows): g = Wg x, u = Wu x
+//   gate/up  per (block, tile of 64 intermediate rows; 128 for the
+//            256-wide and the scaled kernels below): g = Wg x, u = Wu x
 //            on MFMA 16x16x32 bf16 with fp32 accumulation, then
 //            h = silu(g) * u, stored as a bf16 hi + lo pair
-//   down     per (block, tile of 512 hidden rows, 256 for six-bit codes): y = Wd (h_hi + h_lo)
-//            into fp32 partials, one row per (token, expert) pair
+//   down     y = Wd (h_hi + h_lo) into fp32 partials, one row per (token,
+//            expert) pair: for K of 256..512 a persistent grid (one
+//            workgroup per CU) shares out the 256-row passes of every block,
+//            each block's h resident in LDS; otherwise per (block, tile of
+//            512 hidden rows, 256 for six-bit codes)
 //   combine  per token: sum of w_r * y_r in rank order, plus the shared
 //            expert, rounded once to bf16
 //
