@@ -196,8 +196,9 @@ int moe_expert_ffn_q(const moe_layer *L, int expert, const void *x, int M, void 
  *   out[t] = sum_{r<k} w[t][r] * FFN_{idx[t][r]}(x_t) + FFN_shared(x_t)
  * in that order.  idx_out (int32 [T][k]) and w_out (fp32 [T][k]) receive the
  * routing when not NULL.  T <= 16 runs as one kernel launch (decode); larger
- * T runs the grouped-GEMM prefill path (bf16 matrix cores after exact
- * dequantisation in LDS). */
+ * T runs the grouped-GEMM prefill path (bf16 matrix cores on weights
+ * dequantised exactly in registers; with MX activations and MX weights, the
+ * scaled fp8 x fp6/fp4 matrix cores on the codes as stored). */
 int moe_layer_decode(const moe_layer *L, const void *x, const float *logits, int T, void *out,
                      int32_t *idx_out, float *w_out, int flags, void *ws, size_t ws_bytes,
                      void *stream);
