@@ -397,7 +397,7 @@ def main():
         traffic_summary(a)
         return
     if a.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(expert sharding over RCCL is a design note, not code)", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -90,7 +90,7 @@ extern "C" {
 enum {
     MOE_OK = 0,
     MOE_EINVAL = -1,        /* an argument breaks a documented rule */
-    MOE_EUNSUPPORTED = -2,  /* valid, but outside what this build implements */
+    MOE_EUNSUPPORTED = -2,  /* valid, but outside what this library implements */
     MOE_EWORKSPACE = -3,    /* workspace missing, misaligned or too small */
     MOE_EHIP = -4,          /* a HIP runtime call failed (text holds its error) */
     MOE_EKERNEL = -5        /* a kernel's bounded wait expired (moe_workspace_status) */
