@@ -37,6 +37,9 @@ PF_RES = [MoEConfig("pf_res_f%d" % f, tokens=150, hidden=768, experts=6, top_k=2
 # ceil(H / 256)) than CUs, so workgroups take runs of passes that start inside
 # a block and cross into the next; H = 1152 ends in a half-empty pass
 PF_RES_WIDE = MoEConfig("pf_res_wide", tokens=1024, hidden=1152, experts=8, top_k=4, inter=256, shared_inter=256)
+# the largest routing the C ABI takes: 1,024 experts plus the shared one (1,025
+# slots, so the plan builder's threads take two slots each) and top-32
+PF_WIDEST = MoEConfig("pf_widest", tokens=96, hidden=256, experts=1024, top_k=32, inter=256, shared_inter=256)
 _layers = {}
 
 
@@ -99,6 +102,16 @@ def test_prefill_resident_down_runs_of_passes():
     assert np.allclose(w[rows], rw, rtol=1e-6, atol=0)
     assert max_rel_err(out32.cpu().numpy()[rows], ref) <= PARITY_TOL
     assert np.array_equal(host_bf16(out16), bf16_rne_of_f32(out32))
+
+
+def test_prefill_widest_routing():
+    """1,024 routed experts, most of them with a few tokens or none, top-32,
+    and the shared expert: every token against the oracle."""
+    require_gpu()
+    cfg = PF_WIDEST
+    print("prefill widest routing", flush=True)
+    x, l = synth.hidden_states(cfg, sub=43), synth.router_logits(cfg, sub=43)
+    _check(cfg, x, l, *_run(cfg, x, l))
 
 
 @pytest.mark.parametrize("T", [17, 64, 65, 130])
