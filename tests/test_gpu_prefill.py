@@ -3,7 +3,9 @@ against the oracle: several tiles with ragged tails in H, I and the shared
 expert's width, both formats, experts with no tokens and with more tokens
 than one block holds, fixed-expert calls, chunking past 2,048 tokens, and the
 full-size 2,048-token workload on sampled tokens; the down projection with
-the block's h resident in LDS for every weight format."""
+the block's h resident in LDS for every weight format, and its persistent
+grid over runs of passes; the widest routing (1,024 experts + shared, top-32);
+top-1 (bitwise the expert's FFN) and top-E (the dense mixture)."""
 import numpy as np
 import pytest
 import torch
@@ -40,6 +42,8 @@ PF_RES_WIDE = MoEConfig("pf_res_wide", tokens=1024, hidden=1152, experts=8, top_
 # the largest routing the C ABI takes: 1,024 experts plus the shared one (1,025
 # slots, so the plan builder's threads take two slots each) and top-32
 PF_WIDEST = MoEConfig("pf_widest", tokens=96, hidden=256, experts=1024, top_k=32, inter=256, shared_inter=256)
+# the degenerate routings on the many-token path: top-1 and top-E
+PF_DEG = MoEConfig("pf_deg", tokens=40, hidden=256, experts=8, top_k=8, inter=256)
 _layers = {}
 
 
@@ -111,6 +115,33 @@ def test_prefill_widest_routing():
     cfg = PF_WIDEST
     print("prefill widest routing", flush=True)
     x, l = synth.hidden_states(cfg, sub=43), synth.router_logits(cfg, sub=43)
+    _check(cfg, x, l, *_run(cfg, x, l))
+
+
+def test_prefill_top1_equals_expert_ffn_bitwise():
+    """k = 1: each token's output is its expert's FFN (weight exactly 1), the
+    same bits as that expert run over all 40 tokens on the same path (a
+    token's row is multiplied the same way whatever block it sits in)."""
+    require_gpu()
+    cfg = PF_DEG
+    L1 = _layer(cfg).with_top_k(1)
+    x, l = synth.hidden_states(cfg, sub=45), synth.router_logits(cfg, sub=45)
+    xd, ld = dev_bf16(x), torch.from_numpy(np.ascontiguousarray(l)).cuda()
+    idx = torch.empty((cfg.tokens, 1), dtype=torch.int32, device="cuda")
+    out = moeq.moe_layer_decode(L1, xd, ld, idx_out=idx, flags=F32)
+    ie = idx.cpu().numpy()[:, 0]
+    assert np.array_equal(ie, oracle.route(l, 1)[0][:, 0])
+    for e in np.unique(ie):
+        y = moeq.moe_expert_ffn_q(L1, int(e), xd, flags=F32)
+        rows = torch.from_numpy(np.nonzero(ie == e)[0]).cuda()
+        assert torch.equal(y[rows], out[rows]), int(e)
+
+
+def test_prefill_top_e_is_the_dense_mixture():
+    """k = E: every expert serves every token, weights the softmax over all."""
+    require_gpu()
+    cfg = PF_DEG
+    x, l = synth.hidden_states(cfg, sub=46), synth.router_logits(cfg, sub=46)
     _check(cfg, x, l, *_run(cfg, x, l))
 
 
