@@ -145,6 +145,16 @@ def test_prefill_top_e_is_the_dense_mixture():
     _check(cfg, x, l, *_run(cfg, x, l))
 
 
+@pytest.mark.parametrize("E", [100, 200])
+def test_prefill_expert_counts(E):
+    """Expert counts that take the routing's two- and four-logits-per-lane
+    instances (65..128 and 129..256 experts) in the route+group launch."""
+    require_gpu()
+    cfg = MoEConfig("pf_e%d" % E, tokens=70, hidden=256, experts=E, top_k=6, inter=128, shared_inter=64)
+    x, l = synth.hidden_states(cfg, sub=47), synth.router_logits(cfg, sub=47)
+    _check(cfg, x, l, *_run(cfg, x, l))
+
+
 @pytest.mark.parametrize("T", [17, 64, 65, 130])
 def test_prefill_token_counts(T):
     require_gpu()
