@@ -1,6 +1,7 @@
 """The steps either side of the layer on the GPU: RMSNorm, the router scores
 with their fused top-k, and the whole block (norm -> scores -> layer ->
-residual add), against the oracle.
+residual add), against the oracle, also with the activations quantised to MX
+e4m3 on MXFP4 experts.
 
 Where floating point decides an integer -- the bf16 rounding of the
 normalised activation, and which experts the scores select -- the GPU decides
@@ -19,7 +20,7 @@ import block_scaled_bit_moe_amd as moeq
 import oracle
 import synth
 import synth.device
-from gpu_util import bf16_rne_of_f32, dev_bf16, host_bf16, require_gpu, upload_layer
+from gpu_util import bf16_rne_of_f32, dev_bf16, host_bf16, oracle_layer, require_gpu, upload_layer
 from helpers import PARITY_TOL, max_rel_err
 from synth import configs
 from synth.configs import MoEConfig
@@ -175,3 +176,38 @@ def test_full_size_block(cfg):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, eager)
+
+
+# MXFP4 experts with quantised activations through the block call (the
+# quantiser takes the normalised rows; the residual is the raw stream)
+BLK_MX = MoEConfig("blk_mx", tokens=16, hidden=1024, experts=24, top_k=4, inter=256, shared_inter=128, fmt=3,
+                   ue8m0_exp=(-6, -2), logit_sigma=1.5)
+
+
+@pytest.mark.parametrize("T", [1, 16, 40])
+def test_block_with_quantised_activations(T):
+    """moe_block_decode with MOE_ACT_MXFP8 against the oracle: the norm's output
+    taken from moe_rmsnorm (the kernel the block runs, so bitwise its rows),
+    the scores and ranking in double from those rows, the experts on the
+    activations quantised to MX e4m3 and dequantised, plus the residual."""
+    require_gpu()
+    cfg = BLK_MX
+    B = _block(cfg)
+    x = synth.hidden_states(cfg, tokens=T, sub=60 + T)
+    xd = dev_bf16(x)
+    ws = moeq.block_workspace(B, T)
+    idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    mx = moeq.MOE_ACT_MXFP8
+    out32 = moeq.moe_block_decode(B, xd, idx_out=idx, flags=F32 | mx, ws=ws)
+    out16 = moeq.moe_block_decode(B, xd, flags=mx, ws=ws)
+    moeq.moe_workspace_status(ws)
+    xn = host_bf16(moeq.moe_rmsnorm(xd, dev_bf16(synth.norm_gamma(cfg)), cfg.norm_eps))
+    lg = oracle.router_logits(xn, synth.router_weights(cfg))
+    assert _route_margin_ok(lg, cfg.top_k, 1e-5 * np.abs(lg).max()), "seeded scores too close to call"
+    c, s = oracle.quantize_mx_e4m3(xn)
+    xq = oracle.bf16_round(oracle.dequantize_mx_e4m3(c, s))
+    ridx, _, ref = oracle_layer(cfg, xq, lg.astype(np.float32))
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = ref + _bf16_to_f64(x)
+    assert max_rel_err(out32.cpu().numpy(), ref) <= PARITY_TOL
+    assert np.array_equal(host_bf16(out16), bf16_rne_of_f32(out32))
